@@ -1,0 +1,39 @@
+"""CPU oracle for SageAttention-style quantized attention.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import this
+package.  The product path (the HIP library and its Python binding) never calls it,
+and the oracle never imports the product: the two share no code, headers, tables or
+constants.  Inputs come from the separate ``workloads`` generator module.
+
+What the oracle computes, and where each step comes from:
+
+* ``attention_exact`` - the plain definition softmax(Q K^T / sqrt(d)) V in fp64
+  (juejin page "MiniMax H3 接入 SageAttention 实测加速", section 一; Baidu Cloud page
+  "SDPA稠密注意力模式", section 三 part 1).
+* ``quantize`` - K smoothing by its token mean (the "outlier smoothing" of section 一
+  of the juejin page; the sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 1, keeps
+  that mean term in bf16), per-block INT8 codes for Q and K (INT8 for QK^T, juejin
+  section 一), per-channel FP8 e4m3 codes for V (FP8 for PV, same section).
+* ``attention_pipeline`` - the quantized attention: exact int32 QK^T, dequantisation,
+  fp32 online softmax in base 2 over key tiles (the blockwise computation of the
+  bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2), P rounded
+  to FP8 e4m3, PV accumulated, normalised at the end.
+
+Points the pages leave open are fixed by readings that are listed in the module
+docstrings.  Everything is numpy; floating point is fp64 except where the method's
+own precision (fp32 softmax arithmetic, fp32 scales) decides a quantised code, where
+the oracle computes in fp32 as the method does.
+"""
+from .fp8 import e4m3_decode, e4m3_encode, e4m3_table, E4M3_MAX
+from .quant import (QUANT_BLOCK, bf16_round, k_token_mean, quantize_int8_blocks,
+                    quantize_v_fp8, quantize)
+from .attention import (LOG2E, attention_exact, qk_int32, attention_pipeline,
+                        default_sm_scale, rel_l2)
+
+__all__ = [
+    "e4m3_decode", "e4m3_encode", "e4m3_table", "E4M3_MAX",
+    "QUANT_BLOCK", "bf16_round", "k_token_mean", "quantize_int8_blocks",
+    "quantize_v_fp8", "quantize",
+    "LOG2E", "attention_exact", "qk_int32", "attention_pipeline",
+    "default_sm_scale", "rel_l2",
+]

@@ -1,0 +1,184 @@
+"""Exact attention and the quantised attention pipeline.
+
+EXACT (the plain definition): O = softmax(Q K^T * sm_scale) V with sm_scale = 1/sqrt(d),
+evaluated in fp64 with the row maximum subtracted before exp (juejin page
+"MiniMax H3 接入 SageAttention 实测加速", section 一; Baidu Cloud page
+"SDPA稠密注意力模式", section 三 part 1, whose three-line PyTorch function is the
+same definition).
+
+PIPE (the quantised method): INT8 Q.K'^T with exact int32 sums, dequantised by
+q_scale * k_scale * sm_scale, online softmax in fp32 and base 2 over key tiles of T
+keys, P rounded to FP8 e4m3, P.V8 accumulated, normalised at the end, V scales applied
+(juejin section 一 for INT8-QK/FP8-PV; bjdmk page
+"GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2, for computing attention
+block by block without writing the score matrix).
+
+Readings (the pages give none of these details):
+* Keys are visited in ascending tiles of T keys; the running maximum, and therefore
+  each FP8 rounding of P, depends on T, so T is an argument and must equal the tile
+  of the implementation under test.
+* fp32 softmax arithmetic, in this order, for query i and key j (c.f. the
+  correctly rounded fp32 operations written as fp32(.)):
+    L    = fp32(sm_scale * log2(e))             (product formed in fp64)
+    qf_i = fp32(q_scale_i * L)
+    c_ij = fp32(qf_i * k_scale_j)
+    s_ij = fp32(S_ij * c_ij)                     (base-2 logit, S_ij the int32 sum)
+    m    = max(m_prev, max_j s_ij)               (m_prev = -inf before the first tile)
+    nb   = fp32(log2(448)_fp32 - m)
+    p_ij = exp2(fp32(S_ij * c_ij + nb))          (one rounding: a fused multiply-add)
+    alpha= exp2(fp32(m_prev - m))
+  so p_ij = 448 * 2^(s_ij - m): P is mapped onto the full e4m3 range with a static
+  scale of 448, and p8_ij = e4m3(p_ij).  exp2 is evaluated to fp32 (correctly
+  rounded here; an implementation's exp2 may differ by one unit in the last place).
+* l accumulates the unrounded p_ij: l = alpha * l + sum_j p_ij, acc = alpha * acc +
+  sum_j p8_ij * v8_j; O = acc * v_scale / l.  (The 448 cancels between acc and l.)
+  acc and l are kept in fp64 here; they decide no code.
+* Keys at or beyond N do not exist (no padding in the oracle).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .fp8 import e4m3_encode, e4m3_decode
+from .quant import quantize, QUANT_BLOCK
+
+__all__ = ["LOG2E", "default_sm_scale", "attention_exact", "qk_int32",
+           "attention_pipeline", "rel_l2"]
+
+F32 = np.float32
+LOG2E = math.log2(math.e)
+LOG2_448_F32 = F32(math.log2(448.0))
+
+
+def default_sm_scale(d: int) -> float:
+    """fp32(1/sqrt(d)), returned as a Python float holding that fp32 value."""
+    return float(F32(1.0 / math.sqrt(d)))
+
+
+def _rows(n: int, rows):
+    return np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+
+
+def attention_exact(q, k, v, sm_scale=None, rows=None) -> np.ndarray:
+    """fp64 softmax(Q K^T * sm_scale) V.  q, k, v: float32 [B, N, H, d].
+    ``rows`` selects query tokens.  Returns fp64 [B, R, H, d]."""
+    q = np.asarray(q, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    v = np.asarray(v, dtype=F32)
+    B, N, H, d = q.shape
+    sm = default_sm_scale(d) if sm_scale is None else float(sm_scale)
+    r = _rows(N, rows)
+    out = np.empty((B, len(r), H, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kh = k[b, :, h, :].astype(np.float64)
+            vh = v[b, :, h, :].astype(np.float64)
+            for c0 in range(0, len(r), 512):
+                qh = q[b, r[c0:c0 + 512], h, :].astype(np.float64)
+                s = (qh @ kh.T) * sm
+                s -= s.max(axis=1, keepdims=True)
+                p = np.exp(s)
+                out[b, c0:c0 + 512, h, :] = (p @ vh) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def qk_int32(q_codes, k_codes) -> np.ndarray:
+    """Exact S = Q8 K8^T for one head.  q_codes [R, d], k_codes [M, d] int8.
+
+    Formed as an fp64 matrix product of integer-valued operands: every product and
+    partial sum is an integer of magnitude below 2^53 (|S| <= d * 127^2), so the fp64
+    result is exact.  Returns int64."""
+    a = np.asarray(q_codes, dtype=np.float64)
+    bm = np.asarray(k_codes, dtype=np.float64)
+    return (a @ bm.T).astype(np.int64)
+
+
+def _fma_f32(x, c, b):
+    """fp32(x * c + b) with one rounding: x (integer-valued, |x| < 2^24) times the fp32
+    c is exact in fp64, the fp64 sum is then rounded to fp32."""
+    return (x.astype(np.float64) * c.astype(np.float64) + b.astype(np.float64)).astype(F32)
+
+
+def _exp2_f32(x):
+    return np.exp2(np.asarray(x, dtype=F32).astype(np.float64)).astype(F32)
+
+
+def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
+                       quant=None, int8_qk: bool = True, fp8_p: bool = True,
+                       fp8_v: bool = True, smooth_k: bool = True) -> np.ndarray:
+    """Quantised attention.  q, k, v: float32 [B, N, H, d] holding bf16 values.
+
+    ``quant``: the dict of :func:`oracle.quantize` if already computed.  ``rows``:
+    query tokens to evaluate (rows are independent given the quantised K and V).
+    The switches ``int8_qk``, ``fp8_p`` and ``fp8_v`` replace a quantised operand by
+    its exact value; with all three off the pipeline is exact online softmax.
+    Returns fp64 [B, R, H, d]."""
+    q = np.asarray(q, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    v = np.asarray(v, dtype=F32)
+    B, N, H, d = q.shape
+    sm = default_sm_scale(d) if sm_scale is None else float(sm_scale)
+    if quant is None:
+        quant = quantize(q, k, v, smooth_k=smooth_k)
+    r = _rows(N, rows)
+    L = F32(sm * LOG2E)
+    out = np.empty((B, len(r), H, d), dtype=np.float64)
+    T = int(kv_tile)
+    for b in range(B):
+        for h in range(H):
+            if fp8_v:
+                vv = e4m3_decode(quant["v_f8"][b, h]).astype(np.float64)      # [N, d]
+                vs = quant["v_scale"][b, h].astype(np.float64)
+            else:
+                vv = v[b, :, h, :].astype(np.float64)
+                vs = np.ones(d)
+            if int8_qk:
+                kq = quant["k_i8"][b, h]
+                ks = quant["k_scale"][b, h][np.arange(N) // QUANT_BLOCK]        # [N]
+            else:
+                kf = k[b, :, h, :].astype(np.float64)
+            for c0 in range(0, len(r), 256):
+                rr = r[c0:c0 + 256]
+                R = len(rr)
+                if int8_qk:
+                    S = qk_int32(quant["q_i8"][b, h][rr], kq)                 # [R, N]
+                    qs = quant["q_scale"][b, h][rr // QUANT_BLOCK]
+                    qf = (qs * L).astype(F32)                                 # [R]
+                else:
+                    S = (q[b, rr, h, :].astype(np.float64) @ kf.T) * (sm * LOG2E)
+                m = np.full(R, -np.inf, dtype=F32)
+                l = np.zeros(R)
+                acc = np.zeros((R, d))
+                for t0 in range(0, N, T):
+                    t1 = min(N, t0 + T)
+                    if int8_qk:
+                        x = S[:, t0:t1]
+                        c = (qf[:, None] * ks[None, t0:t1]).astype(F32)       # [R, t]
+                        s = (x.astype(np.float64) * c).astype(F32)
+                    else:
+                        s = S[:, t0:t1].astype(F32)
+                    m_new = np.maximum(m, s.max(axis=1))
+                    nb = (LOG2_448_F32 - m_new).astype(F32)
+                    if int8_qk:
+                        arg = _fma_f32(x, c, np.broadcast_to(nb[:, None], x.shape))
+                    else:
+                        arg = (s.astype(np.float64) + nb[:, None]).astype(F32)
+                    p = _exp2_f32(arg)                                        # [R, t]
+                    with np.errstate(invalid="ignore"):
+                        alpha = _exp2_f32((m - m_new).astype(F32)).astype(np.float64)
+                    alpha = np.where(np.isneginf(m), 0.0, alpha)
+                    pq = e4m3_decode(e4m3_encode(p)) if fp8_p else p.astype(np.float64)
+                    l = alpha * l + p.astype(np.float64).sum(axis=1)
+                    acc = alpha[:, None] * acc + pq @ vv[t0:t1]
+                    m = m_new
+                out[b, c0:c0 + R, h, :] = acc * vs[None, :] / l[:, None]
+    return out
+
+
+def rel_l2(a, b) -> float:
+    """||a - b||_2 / ||b||_2 in fp64."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))

@@ -1,0 +1,160 @@
+"""Pins of the oracle's attention: exact attention by brute force and invariants, the
+quantised pipeline against the exact definition with quantisation switched off, closed
+forms, and sanity bounds on the quantisation error."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import attention_exact, attention_pipeline, qk_int32, rel_l2
+
+F32 = np.float32
+
+
+def _qkv(B, N, H, d, seed, kbias=0.0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).float().numpy()
+    k = (torch.randn(B, N, H, d, generator=g) + kbias).to(torch.bfloat16).float().numpy()
+    v = torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).float().numpy()
+    return q, k, v
+
+
+def _exact_loops(q, k, v, sm):
+    """Literal scalar definition with math.fsum, one (b, h) at a time."""
+    B, N, H, d = q.shape
+    out = np.zeros((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                s = [sm * math.fsum(float(q[b, i, h, c]) * float(k[b, j, h, c]) for c in range(d))
+                     for j in range(N)]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                z = math.fsum(e)
+                for c in range(d):
+                    out[b, i, h, c] = math.fsum(e[j] * float(v[b, j, h, c]) for j in range(N)) / z
+    return out
+
+
+@pytest.mark.parametrize("N,d", [(1, 4), (2, 4), (3, 4), (63, 4), (64, 4), (65, 4), (130, 4), (3, 64), (65, 64)])
+def test_exact_equals_scalar_definition(N, d):
+    q, k, v = _qkv(1, N, 2 if N < 100 else 1, d, seed=N * 10 + d)
+    sm = oracle.default_sm_scale(d)
+    assert np.abs(attention_exact(q, k, v) - _exact_loops(q, k, v, sm)).max() < 1e-13
+
+
+def test_exact_single_token_returns_v():
+    q, k, v = _qkv(2, 1, 3, 16, seed=5)
+    assert np.array_equal(attention_exact(q, k, v), v.astype(np.float64))
+
+
+def test_exact_rows_are_convex_weights():
+    # V = identity: the output rows are the softmax rows themselves
+    N = 32
+    q, k, _ = _qkv(1, N, 1, N, seed=6)
+    v = np.eye(N, dtype=F32)[None, :, None, :]
+    p = attention_exact(q, k, v)[0, :, 0, :]
+    assert np.all(p > 0)
+    assert np.abs(p.sum(axis=1) - 1).max() < N * 2.0 ** -52 * 4
+
+
+@pytest.mark.parametrize("shift", ["mean", "random"])
+def test_exact_invariant_to_key_shift(shift):
+    q, k, v = _qkv(1, 100, 2, 32, seed=7, kbias=3.0)
+    # shifts with few significant bits, so that K - c is exact in fp32
+    if shift == "mean":
+        c = oracle.k_token_mean(k)[:, None]                      # the smoothing mean, bf16
+    else:
+        c = np.round(np.random.default_rng(0).standard_normal((1, 1, 2, 32)) * 20) / 4
+    kc = k.astype(np.float64) - c
+    assert np.array_equal(kc.astype(F32).astype(np.float64), kc)
+    a = attention_exact(q, k, v)
+    b = attention_exact(q, kc, v)
+    assert rel_l2(b, a) < 1e-12
+
+
+def test_qk_int32_fp64_product_is_exact():
+    rng = np.random.default_rng(3)
+    a = rng.integers(-127, 128, (40, 128)).astype(np.int8)
+    b = rng.integers(-127, 128, (50, 128)).astype(np.int8)
+    a[0] = 127
+    b[0] = 127
+    b[1] = -127
+    ref = a.astype(np.int64) @ b.astype(np.int64).T
+    got = qk_int32(a, b)
+    assert np.array_equal(got, ref)
+    assert got[0, 0] == 128 * 127 * 127
+
+
+@pytest.mark.parametrize("T", [16, 64, 128, 1000])
+def test_pipeline_without_quantisation_is_exact_softmax(T):
+    q, k, v = _qkv(1, 300, 2, 64, seed=8, kbias=2.0)
+    ex = attention_exact(q, k, v)
+    pp = attention_pipeline(q, k, v, kv_tile=T, int8_qk=False, fp8_p=False, fp8_v=False)
+    # the only rounding left is the fp32 base-2 logit and exp2
+    assert np.abs(pp - ex).max() < 2e-6
+
+
+def test_pipeline_normalisation_with_constant_v():
+    # V = 1 everywhere: with unrounded P the output is sum(p) / l = 1 exactly
+    q, k, v = _qkv(1, 200, 2, 16, seed=9, kbias=3.0)
+    ones = np.ones_like(v)
+    o = attention_pipeline(q, k, ones, kv_tile=64, fp8_p=False, fp8_v=False)
+    assert np.abs(o - 1).max() < 1e-12
+    # with P in e4m3 the output is sum(p8)/sum(p): within the e4m3 relative step
+    o8 = attention_pipeline(q, k, ones, kv_tile=64)
+    assert np.abs(o8 - 1).max() < 2.0 ** -4
+
+
+def test_pipeline_uniform_case_closed_form():
+    # identical key rows: K' = 0, S = 0, every p equals 448 (up to exp2 rounding),
+    # and the output is the token mean of the dequantised V
+    q, k, v = _qkv(1, 150, 2, 32, seed=10)
+    k[:] = k[:, :1]
+    quant = oracle.quantize(q, k, v)
+    assert not quant["k_i8"].any()
+    o = attention_pipeline(q, k, v, kv_tile=64, quant=quant)
+    vd = oracle.e4m3_decode(quant["v_f8"]) * quant["v_scale"][:, :, None, :]
+    want = vd.mean(axis=2)                                   # [B, H, d]
+    assert np.abs(o - want[:, None]).max() < 1e-6 * np.abs(want).max()
+    # Q = 0 gives the same uniform weights
+    _, k_rand, _ = _qkv(1, 150, 2, 32, seed=13, kbias=2.0)
+    o0 = attention_pipeline(np.zeros_like(q), k_rand, v, kv_tile=64)
+    assert np.abs(o0 - want[:, None]).max() < 1e-6 * np.abs(want).max()
+
+
+def test_pipeline_rows_subset_is_bitwise_consistent():
+    q, k, v = _qkv(1, 333, 2, 64, seed=11, kbias=3.0)
+    full = attention_pipeline(q, k, v)
+    rows = [0, 5, 64, 200, 332]
+    sub = attention_pipeline(q, k, v, rows=rows)
+    assert np.array_equal(sub, full[:, rows])
+
+
+def _golden(name):
+    path = os.path.join(os.path.dirname(__file__), "golden", "pages_accuracy.txt")
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            key, val = line.split()
+            if key == name:
+                return float(val)
+    raise KeyError(name)
+
+
+def test_error_budget_sanity_on_tiny_workload():
+    w = workloads.get("tiny")
+    q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+    ex = attention_exact(q, k, v)
+    full = rel_l2(attention_pipeline(q, k, v), ex)
+    int8_only = rel_l2(attention_pipeline(q, k, v, fp8_p=False, fp8_v=False), ex)
+    int8_raw = rel_l2(attention_pipeline(q, k, v, fp8_p=False, fp8_v=False, smooth_k=False), ex)
+    # full-key INT8 without smoothing: the page's ratio implies about 0.008 * 3.7
+    implied = _golden("block_residual_k_rel_l2") * _golden("full_key_int8_closeness_ratio")
+    assert implied / 2 < int8_raw < implied * 2
+    assert int8_only < int8_raw                      # smoothing helps
+    # FP8 rounding of P and V (relative step 2^-3) dominates the full pipeline
+    assert 0.02 < full < 0.06
