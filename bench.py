@@ -1,0 +1,188 @@
+"""Throughput of the quantized attention hot path on one MI355X.
+
+A step is one sage_attn_fwd call (quantisation pass + fused attention) over the
+seeded synthetic Flux-like workload (B=1, H=24, N=4608, d=128) with inputs resident in
+HBM.  Prints one JSON line: whole-step TOPS (4*B*H*N^2*d per step), the attention
+kernel's matrix-core roofline fraction, the quantisation pass's HBM rate, the same
+figures at N=16384 and N=65536, and the CPU oracle timed on a bounded sample.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
+                [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = 5000.0        # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s), x1000
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+SWEEP = ["sweep16k", "stress"]
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux_like")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def quant_bytes(w) -> float:
+    """Algorithmic bytes of the quantisation pass: read Q, K, V once (bf16), write the
+    INT8 Q/K and FP8 V codes once; scales and means are < 0.1% and not counted."""
+    E = w.B * w.H * w.N * w.d
+    return 9.0 * E
+
+
+def measure(w, steps, warmup):
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
+    out = torch.empty_like(q)
+    ws = torch.empty(sage.sage_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # whole step
+    for _ in range(warmup):
+        sage.sage_attn_fwd(q, k, v, out=out, workspace=ws)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(steps):
+        sage.sage_attn_fwd(q, k, v, out=out, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / steps
+
+    # the two passes alone, each timed with events on the stream the library uses
+    quant = sage.sage_quant_qk(q, k, v)
+    for _ in range(warmup):
+        sage.sage_quant_qk(q, k, v, out=quant)
+        sage.sage_attn_fwd_prequant(quant, out=out)
+    torch.cuda.synchronize(dev)
+    e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+    e0.record(stream)
+    for _ in range(steps):
+        sage.sage_quant_qk(q, k, v, out=quant)
+    e1.record(stream)
+    e2.record(stream)
+    for _ in range(steps):
+        sage.sage_attn_fwd_prequant(quant, out=out)
+    e3.record(stream)
+    torch.cuda.synchronize(dev)
+    quant_ms = e0.elapsed_time(e1) / steps
+    attn_ms = e2.elapsed_time(e3) / steps
+    del q, k, v, out, ws, quant
+    torch.cuda.empty_cache()
+    return dict(step_ms=step_ms, wall_s=wall, quant_ms=quant_ms, attn_ms=attn_ms,
+                tops=w.ops / (step_ms * 1e-3) / 1e12,
+                attn_tops=w.ops / (attn_ms * 1e-3) / 1e12,
+                quant_gbs=quant_bytes(w) / (quant_ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(w):
+    """The CPU oracle (numpy) on a bounded sample of the workload: the full
+    quantisation of Q, K and V, plus the quantised attention of a sample of query rows
+    in every head; scaled to the whole workload linearly in rows."""
+    import numpy as np
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+
+    q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+    rows = np.linspace(0, w.N - 1, 16).astype(np.int64)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        quant = oracle.quantize(q, k, v)
+        t1 = time.perf_counter()
+        oracle.attention_pipeline(q, k, v, kv_tile=128, rows=rows, quant=quant)
+        t2 = time.perf_counter()
+    est = (t1 - t0) + (t2 - t1) * w.N / len(rows)
+    return {"value": round(w.ops / est / 1e12, 8), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": (f"{w.name}: full quantisation ({t1 - t0:.1f} s) + attention of "
+                       f"{len(rows)} of {w.N} query rows in all {w.H} heads ({t2 - t1:.1f} s), "
+                       f"scaled by rows to {est:.0f} s per step; numpy, 1 thread")}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); heads would be "
+              "sharded across GPUs with no communication, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    sage.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = workloads.get(args.workload)
+    print(f"[bench] {w.name} B={w.B} H={w.H} N={w.N} d={w.d}: {args.warmup} warmup + {args.steps} steps",
+          file=sys.stderr, flush=True)
+    r = measure(w, args.steps, args.warmup)
+    sweep = {}
+    if not args.no_sweep:
+        for name in SWEEP:
+            ws = workloads.get(name)
+            print(f"[bench] sweep {name} N={ws.N}", file=sys.stderr, flush=True)
+            rs = measure(ws, max(3, args.steps // 4), 2)
+            sweep[name] = {"N": ws.N, "H": ws.H, "ms_per_step": round(rs["step_ms"], 4),
+                           "tops": round(rs["tops"], 2), "attn_ms": round(rs["attn_ms"], 4),
+                           "attn_tops": round(rs["attn_tops"], 2),
+                           "mfma_util": round(rs["attn_tops"] / PEAK_TOPS, 4),
+                           "quant_ms": round(rs["quant_ms"], 4),
+                           "quant_gbs": round(rs["quant_gbs"], 1)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+    info = sage.sage_kernel_info()
+    line = {
+        "metric": "quantized-attention TOPS (4*B*H*N^2*d per step: quantisation + attention)",
+        "value": round(r["tops"], 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 QK^T + fp8 PV (fp32 softmax, bf16 io)",
+        "data": "synthetic (seeded N(0,1) Q/V, K with N(0,9) channel bias)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "kv_tile": info["kv_tile"], "block_m": info["block_m"]},
+        "attn_only": {"ms": round(r["attn_ms"], 5), "tops": round(r["attn_tops"], 2),
+                      "mfma_util": round(r["attn_tops"] / PEAK_TOPS, 4)},
+        "quant_only": {"ms": round(r["quant_ms"], 5), "gbs": round(r["quant_gbs"], 1),
+                       "hbm_frac": round(r["quant_gbs"] / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(r["attn_tops"] / PEAK_TOPS, 4),
+                     "traffic": None},
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

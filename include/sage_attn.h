@@ -1,0 +1,166 @@
+/*
+ * sage_attn.h - C ABI of the gfx950 (MI355X) quantized-attention library.
+ *
+ * Computes O = softmax(Q K^T * sm_scale) V, sm_scale normally 1/sqrt(d), with the
+ * low-bit scheme of SageAttention as the pages describe it: Q.K^T in INT8 after the
+ * K "outlier smoothing", P.V in FP8 (juejin page "MiniMax H3 接入 SageAttention 实测加速",
+ * section 一), the K mean term kept in bf16 and only the remainder quantised
+ * (sd114.wiki page on ComfyUI-sol-attn, "核心亮点" item 1), computed block by block
+ * without materialising the N x N score matrix (bjdmk page
+ * "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers of the calling process's current HIP
+ *   device.  bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ * - Q, K, V and O are addressed as logical [B][H][N][d] views through sage_strides
+ *   (element strides of the b, h and n dimensions; the channel dimension must be
+ *   contiguous).  This covers [B, N, H, d] tensors, [B, H, N, d] tensors and the
+ *   strided q/k/v slices of a fused qkv projection without copies (the zero-copy
+ *   reading of fused qkv on the sd114.wiki page, "核心亮点" item 2).
+ * - Quantised operands use fixed layouts, padded to Npad = sage_padded_tokens(N)
+ *   tokens; padding rows hold zero codes and padding scale blocks hold 0:
+ *     q_i8, k_i8   int8    [B][H][Npad][d]
+ *     v_f8         uint8   [B][H][d][Npad]   (channel-major: row c holds V[:, c])
+ *     q_scale, k_scale float [B][H][Npad/64]  (one per block of 64 tokens)
+ *     k_mean       bf16    [B][H][d]
+ *     v_scale      float   [B][H][d]
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null stream).
+ *   They never synchronise and never allocate: scratch memory is passed in by the
+ *   caller.  Inputs are read-only; outputs must not overlap inputs.  One workspace
+ *   must not be used by two calls that can run concurrently.
+ * - Every argument is validated on the host before any HIP call.  A non-zero status
+ *   leaves every output untouched (except SAGE_EHIP, returned when a launch fails);
+ *   sage_last_error() then returns a description (thread-local, valid until the
+ *   calling thread's next call).  There is no fallback path inside the library.
+ * - Supported: d in {64, 128}; 1 <= N <= SAGE_MAX_TOKENS; B, H >= 1; non-causal
+ *   attention without a mask (diffusion transformers attend bidirectionally).
+ *   Base pointers of bf16 views must be 16-byte aligned and their strides multiples
+ *   of 8 elements (128-bit loads); quantised buffers, scratch and workspace must be
+ *   256-byte aligned.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_QUANT_BLOCK 64    /* tokens per Q/K scale block */
+#define SAGE_TOKEN_ALIGN 128   /* Npad is N rounded up to this */
+#define SAGE_MAX_TOKENS (1 << 22)
+
+typedef struct sage_strides {
+    int64_t b, h, n;           /* element strides; channel stride is 1 */
+} sage_strides;
+
+enum {
+    SAGE_OK = 0,
+    SAGE_EINVAL = -1,          /* null pointer, bad size, overlap, bad sm_scale */
+    SAGE_EUNSUPPORTED = -2,    /* d not in {64,128}, N too large, grid too large */
+    SAGE_EALIGN = -3,          /* misaligned pointer or stride */
+    SAGE_EWORKSPACE = -4,      /* workspace/scratch missing, short or misaligned */
+    SAGE_EHIP = -5             /* a kernel launch failed (HIP error text in sage_last_error) */
+};
+
+typedef struct sage_info {
+    int block_m;               /* query rows per attention workgroup */
+    int kv_tile;               /* keys per online-softmax step (the tile T) */
+    int quant_block;           /* tokens per Q/K scale block */
+    int token_align;           /* Npad alignment */
+    float p_scale;             /* static scale of P before its e4m3 rounding (448) */
+    int d_supported_mask;      /* bit (d/64 - 1) set for each supported head dim */
+    char arch[16];             /* "gfx950" */
+} sage_info;
+
+/* Description of the last failing call on this thread ("" if none). */
+const char* sage_last_error(void);
+
+/* Compile-time parameters of the kernels.  Returns SAGE_OK (SAGE_EINVAL on NULL). */
+int sage_kernel_info(sage_info* info);
+
+/* Npad: N rounded up to SAGE_TOKEN_ALIGN (0 for N <= 0). */
+int64_t sage_padded_tokens(int N);
+
+/* Bytes of scratch sage_quant_qk needs (fp64 partial sums of K, V max partials,
+ * 1/scale factors of V), and bytes of workspace sage_attn_fwd needs (all quantised
+ * operands plus that scratch).  Status as for the calls they size. */
+int sage_quant_scratch_bytes(int B, int H, int N, int d, size_t* bytes);
+int sage_workspace_bytes(int B, int H, int N, int d, size_t* bytes);
+
+/*
+ * sage_quant_qk - the quantisation pass.
+ *   k_mean[b,h,c] = bf16(fp32(sum_t K[b,h,t,c] / N))  (sum over the N valid tokens, fp64)
+ *   Q, and K' = fp32(K) - fp32(k_mean), are coded per block of 64 tokens:
+ *     scale = amax/127, code = clamp(rint(x * (127/amax)), -127, 127) (rint: half to even)
+ *   V is coded per (b, h, channel): v_scale = vamax/448, code = e4m3(v * (448/vamax)),
+ *     e4m3 rounding to nearest even, saturating.
+ *   amax = 0 gives scale 0 and zero codes.
+ * Inputs q, k, v: bf16 [B][H][N][d] views (strides sq, sk, sv).
+ * Outputs: the quantised layouts above, all allocated by the caller.
+ * scratch: >= sage_quant_scratch_bytes() bytes, 256-byte aligned.
+ * Sources: K smoothing and INT8 for QK^T, FP8 for PV (juejin page section 一);
+ * mean term kept in bf16 (sd114.wiki page "核心亮点" item 1).
+ */
+int sage_quant_qk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const sage_strides* sq, const sage_strides* sk, const sage_strides* sv,
+                  int B, int H, int N, int d,
+                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                  uint16_t* k_mean, uint8_t* v_f8, float* v_scale,
+                  void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * sage_attn_fwd_prequant - fused attention on quantised operands.
+ * For each query i, keys are visited in tiles of kv_tile (sage_kernel_info) keys:
+ *   S = q_i8 . k_i8^T exactly in int32 (INT8 matrix cores),
+ *   base-2 logits s = S * fp32(fp32(q_scale*fp32(sm_scale*log2 e)) * k_scale),
+ *   fp32 online softmax with exp2 (running max m, p = 448 * 2^(s - m)),
+ *   P rounded to e4m3, acc += P8 . V8 (FP8 matrix cores, fp32 accumulation),
+ *   l accumulates the unrounded p; O = acc * v_scale / l, written as bf16 (RNE)
+ *   through the [B][H][N][d] view `out` (strides so).
+ * Keys and queries at index >= N are never read as data: keys are masked, rows
+ * beyond N are not written.  sm_scale must be finite and > 0.
+ */
+int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
+                           const int8_t* k_i8, const float* k_scale,
+                           const uint8_t* v_f8, const float* v_scale,
+                           uint16_t* out, const sage_strides* so,
+                           int B, int H, int N, int d, float sm_scale, void* stream);
+
+/*
+ * sage_attn_fwd - the whole hot path: sage_quant_qk into the workspace, then
+ * sage_attn_fwd_prequant.  strides[0..3] describe q, k, v and out.
+ * workspace: >= sage_workspace_bytes() bytes, 256-byte aligned.  After the call
+ * the workspace holds the quantised operands in this order, each region starting
+ * on a 256-byte boundary: q_i8, k_i8, v_f8, q_scale, k_scale, k_mean, v_scale.
+ */
+int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                  int B, int H, int N, int d, float sm_scale,
+                  const sage_strides strides[4], void* stream,
+                  void* workspace, size_t workspace_bytes);
+
+/*
+ * sage_debug_qk_i32 - diagnostic: the exact int32 S = Q8.K8^T tiles of head (b, h),
+ * computed by the same staging and matrix-core code as the attention kernel.
+ * Covers query rows [q_block*block_m, (q_block+n_q_blocks)*block_m) and keys
+ * [kv_tile*T, (kv_tile+n_kv_tiles)*T) of the padded operands; s_out is int32,
+ * row-major [n_q_blocks*block_m][n_kv_tiles*T].  Tiles must lie inside Npad.
+ */
+int sage_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                      int b, int h, int q_block, int kv_tile, int n_q_blocks, int n_kv_tiles,
+                      int32_t* s_out, void* stream);
+
+/*
+ * sage_debug_e4m3 - diagnostic: the device fp32 -> e4m3 conversion the quantisation
+ * kernel uses for V (round to nearest even, saturating to +-448), on n values.
+ */
+int sage_debug_e4m3(const float* x, uint8_t* codes, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

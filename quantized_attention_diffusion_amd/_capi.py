@@ -1,0 +1,257 @@
+"""ctypes binding of libsage_attn.so.  Argument marshalling only: every step of the
+computation runs in the library's HIP kernels; torch supplies device memory and the
+current stream.  The functions carry the C entry points' names."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["SageError", "lib_path", "load", "sage_last_error", "sage_kernel_info",
+           "sage_padded_tokens", "sage_workspace_bytes", "sage_quant_scratch_bytes",
+           "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd", "sage_debug_qk_i32",
+           "sage_debug_e4m3", "EXPORTS", "STATUS"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(HERE, "libsage_attn.so")
+
+STATUS = {0: "SAGE_OK", -1: "SAGE_EINVAL", -2: "SAGE_EUNSUPPORTED", -3: "SAGE_EALIGN",
+          -4: "SAGE_EWORKSPACE", -5: "SAGE_EHIP"}
+
+EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
+           "sage_quant_scratch_bytes", "sage_workspace_bytes", "sage_quant_qk",
+           "sage_attn_fwd_prequant", "sage_attn_fwd", "sage_debug_qk_i32", "sage_debug_e4m3"]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+
+
+class sage_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class sage_info(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("kv_tile", ctypes.c_int),
+                ("quant_block", ctypes.c_int), ("token_align", ctypes.c_int),
+                ("p_scale", ctypes.c_float), ("d_supported_mask", ctypes.c_int),
+                ("arch", ctypes.c_char * 16)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "sage_last_error": (ctypes.c_char_p, []),
+    "sage_kernel_info": (_I, [ctypes.POINTER(sage_info)]),
+    "sage_padded_tokens": (ctypes.c_int64, [_I]),
+    "sage_quant_scratch_bytes": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "sage_workspace_bytes": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "sage_quant_qk": (_I, [_P, _P, _P, ctypes.POINTER(sage_strides), ctypes.POINTER(sage_strides),
+                           ctypes.POINTER(sage_strides), _I, _I, _I, _I,
+                           _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sage_attn_fwd_prequant": (_I, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(sage_strides),
+                                    _I, _I, _I, _I, ctypes.c_float, _P]),
+    "sage_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
+                           ctypes.POINTER(sage_strides), _P, _P, _SZ]),
+    "sage_debug_qk_i32": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "sage_debug_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
+}
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises if it has not been built: there is no other path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is missing: build it with "
+                              "`python -m quantized_attention_diffusion_amd.build`")
+        lib = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SageError(status, sage_last_error())
+
+
+def sage_last_error() -> str:
+    return load().sage_last_error().decode()
+
+
+def sage_kernel_info() -> dict:
+    info = sage_info()
+    _check(load().sage_kernel_info(ctypes.byref(info)))
+    return dict(block_m=info.block_m, kv_tile=info.kv_tile, quant_block=info.quant_block,
+                token_align=info.token_align, p_scale=info.p_scale,
+                d_supported=[64 * (i + 1) for i in range(8) if info.d_supported_mask >> i & 1],
+                arch=info.arch.decode())
+
+
+def sage_padded_tokens(N: int) -> int:
+    return int(load().sage_padded_tokens(N))
+
+
+def sage_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    n = _SZ()
+    _check(load().sage_workspace_bytes(B, H, N, d, ctypes.byref(n)))
+    return n.value
+
+
+def sage_quant_scratch_bytes(B: int, H: int, N: int, d: int) -> int:
+    n = _SZ()
+    _check(load().sage_quant_scratch_bytes(B, H, N, d, ctypes.byref(n)))
+    return n.value
+
+
+# ------------------------------------------------------------------ marshalling
+def _dims(t: torch.Tensor, layout: str):
+    """(B, H, N, d) and the element strides of a 4-D view in ``layout`` ('bnhd' or
+    'bhnd')."""
+    if t.dim() != 4:
+        raise ValueError(f"expected a 4-D tensor, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError("the channel dimension must be contiguous")
+    if layout == "bnhd":
+        B, N, H, d = t.shape
+        st = sage_strides(t.stride(0), t.stride(2), t.stride(1))
+    elif layout == "bhnd":
+        B, H, N, d = t.shape
+        st = sage_strides(t.stride(0), t.stride(1), t.stride(2))
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    return (B, H, N, d), st
+
+
+def _bf16_cuda(name, t):
+    if t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a bfloat16 CUDA tensor (got {t.dtype} on {t.device})")
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _alloc_quant(B, H, N, d, dev):
+    npad = sage_padded_tokens(N)
+    nblk = npad // 64
+    return dict(
+        q_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
+        q_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+        k_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
+        k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+        k_mean=torch.empty((B, H, d), dtype=torch.bfloat16, device=dev),
+        v_f8=torch.empty((B, H, d, npad), dtype=torch.uint8, device=dev),
+        v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+    )
+
+
+def sage_quant_qk(q, k, v, layout: str = "bnhd", out: dict | None = None,
+                  scratch: torch.Tensor | None = None) -> dict:
+    """Quantise Q, K, V (bf16 CUDA views in ``layout``).  Returns the dict of quantised
+    operands (padded layouts of the C header) plus 'N'."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _bf16_cuda(n, t)
+    (B, H, N, d), sq = _dims(q, layout)
+    dk, sk = _dims(k, layout)
+    dv, sv = _dims(v, layout)
+    if dk != (B, H, N, d) or dv != (B, H, N, d):
+        raise ValueError("q, k and v must have the same shape")
+    dev = q.device
+    o = out if out is not None else _alloc_quant(B, H, N, d, dev)
+    if scratch is None:
+        scratch = torch.empty(sage_quant_scratch_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    _check(load().sage_quant_qk(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sq), ctypes.byref(sk),
+        ctypes.byref(sv), B, H, N, d,
+        o["q_i8"].data_ptr(), o["q_scale"].data_ptr(), o["k_i8"].data_ptr(),
+        o["k_scale"].data_ptr(), o["k_mean"].data_ptr(), o["v_f8"].data_ptr(),
+        o["v_scale"].data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(dev)))
+    o["N"] = N
+    return o
+
+
+def _default_scale(d: int) -> float:
+    return float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+
+
+def sage_attn_fwd_prequant(quant: dict, out: torch.Tensor | None = None,
+                           sm_scale: float | None = None, layout: str = "bnhd") -> torch.Tensor:
+    """Attention on operands produced by :func:`sage_quant_qk`.  Returns ``out``."""
+    B, H, npad, d = quant["q_i8"].shape
+    N = int(quant["N"])
+    dev = quant["q_i8"].device
+    if out is None:
+        shape = (B, N, H, d) if layout == "bnhd" else (B, H, N, d)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _bf16_cuda("out", out)
+    dims, so = _dims(out, layout)
+    if dims != (B, H, N, d):
+        raise ValueError(f"out has dims {dims}, expected {(B, H, N, d)}")
+    sm = _default_scale(d) if sm_scale is None else float(sm_scale)
+    _check(load().sage_attn_fwd_prequant(
+        quant["q_i8"].data_ptr(), quant["q_scale"].data_ptr(), quant["k_i8"].data_ptr(),
+        quant["k_scale"].data_ptr(), quant["v_f8"].data_ptr(), quant["v_scale"].data_ptr(),
+        out.data_ptr(), ctypes.byref(so), B, H, N, d, sm, _stream(dev)))
+    return out
+
+
+def sage_attn_fwd(q, k, v, out: torch.Tensor | None = None, sm_scale: float | None = None,
+                  layout: str = "bnhd", workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """O = softmax(Q K^T * sm_scale) V by the quantised path.  q, k, v, out: bf16 CUDA
+    views in ``layout`` ('bnhd' = [B, N, H, d], 'bhnd' = [B, H, N, d]); any strides with
+    a contiguous channel dimension (e.g. slices of a fused qkv tensor)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _bf16_cuda(n, t)
+    (B, H, N, d), sq = _dims(q, layout)
+    dk, sk = _dims(k, layout)
+    dv, sv = _dims(v, layout)
+    if dk != (B, H, N, d) or dv != (B, H, N, d):
+        raise ValueError("q, k and v must have the same shape")
+    dev = q.device
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    _bf16_cuda("out", out)
+    do, so = _dims(out, layout)
+    if do != (B, H, N, d):
+        raise ValueError("out must have the shape of q")
+    if workspace is None:
+        workspace = torch.empty(sage_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    sm = _default_scale(d) if sm_scale is None else float(sm_scale)
+    strides = (sage_strides * 4)(sq, sk, sv, so)
+    _check(load().sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                B, H, N, d, sm, strides, _stream(dev), workspace.data_ptr(),
+                                workspace.numel()))
+    return out
+
+
+def sage_debug_qk_i32(q_i8, k_i8, N: int, b: int, h: int, q_block: int, kv_tile: int,
+                      n_q_blocks: int = 1, n_kv_tiles: int = 1) -> torch.Tensor:
+    """Int32 S tiles of head (b, h) from the quantised operands (see the C header)."""
+    B, H, npad, d = q_i8.shape
+    info = sage_kernel_info()
+    s = torch.empty((n_q_blocks * info["block_m"], n_kv_tiles * info["kv_tile"]),
+                    dtype=torch.int32, device=q_i8.device)
+    _check(load().sage_debug_qk_i32(q_i8.data_ptr(), k_i8.data_ptr(), B, H, N, d, b, h,
+                                    q_block, kv_tile, n_q_blocks, n_kv_tiles, s.data_ptr(),
+                                    _stream(q_i8.device)))
+    return s
+
+
+def sage_debug_e4m3(x: torch.Tensor) -> torch.Tensor:
+    """Device fp32 -> e4m3 codes (the conversion used for V)."""
+    if x.dtype != torch.float32 or x.device.type != "cuda" or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 CUDA tensor")
+    y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(load().sage_debug_e4m3(x.data_ptr(), y.data_ptr(), x.numel(), _stream(x.device)))
+    return y

@@ -1,0 +1,66 @@
+// Internal declarations shared by the gfx950 kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+constexpr int kQuantBlock = 64;     // tokens per Q/K scale block
+constexpr int kTokenAlign = 128;    // Npad alignment (one key tile)
+constexpr int kKvTile = 128;        // keys per online-softmax step
+constexpr int kWaves = 4;           // waves per attention workgroup
+constexpr int kGroupsPerWave = 2;   // 16-query groups per wave
+constexpr int kBlockM = kWaves * kGroupsPerWave * 16;   // 128 query rows per workgroup
+constexpr float kPScale = 448.0f;   // static scale of P before e4m3 rounding
+constexpr int kStatsChunk = 256;    // tokens per partial-sum chunk of the quantisation pass
+
+struct Strides { int64_t b, h, n; };
+
+inline int64_t padded_tokens(int n) {
+  return n <= 0 ? 0 : ((int64_t)n + kTokenAlign - 1) / kTokenAlign * kTokenAlign;
+}
+inline int stats_chunks(int n) { return (n + kStatsChunk - 1) / kStatsChunk; }
+
+// Operands of the quantisation pass.
+struct QuantArgs {
+  const uint16_t *q, *k, *v;
+  Strides sq, sk, sv;
+  int B, H, N, d;
+  int64_t npad;
+  int8_t* q_i8;
+  float* q_scale;
+  int8_t* k_i8;
+  float* k_scale;
+  uint16_t* k_mean;
+  uint8_t* v_f8;
+  float* v_scale;
+  double* ksum_part;   // [B*H][chunks][d]
+  float* vmax_part;    // [B*H][chunks][d]
+  float* v_inv;        // [B*H][d]
+};
+
+// Operands of the fused attention kernel.
+struct AttnArgs {
+  const int8_t* q_i8;
+  const float* q_scale;
+  const int8_t* k_i8;
+  const float* k_scale;
+  const uint8_t* v_f8;
+  const float* v_scale;
+  uint16_t* out;
+  Strides so;
+  int B, H, N, d;
+  int64_t npad;
+  float log2e_scale;   // fp32(sm_scale * log2(e))
+  float log2_pscale;   // fp32(log2(448))
+};
+
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_t npad,
+                           int64_t bh, int q_block, int kv_tile, int n_q_blocks,
+                           int n_kv_tiles, int32_t* s_out, hipStream_t s);
+hipError_t launch_debug_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t s);
+
+}  // namespace sage

@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point the header declares, and rejects bad arguments with the documented status
+before making any HIP call (fake device addresses are safe here for that reason)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from quantized_attention_diffusion_amd import _capi
+    if not os.path.exists(_capi.lib_path):
+        from quantized_attention_diffusion_amd import build
+        build.build()
+    return _capi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    from quantized_attention_diffusion_amd import _capi
+    declared = _declared()
+    assert declared == sorted(_capi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _st(b, h, n):
+    from quantized_attention_diffusion_amd._capi import sage_strides
+    return sage_strides(b, h, n)
+
+
+A = 1 << 32           # fake, 256-byte aligned device addresses: never dereferenced
+B_ = 2 << 32
+C = 3 << 32
+O = 4 << 32
+W = 5 << 32
+
+
+def _fwd(lib, q=A, k=B_, v=C, o=O, B=1, H=2, N=100, d=128, sm=0.088, strides=None, ws=W, wsb=None):
+    from quantized_attention_diffusion_amd._capi import sage_strides
+    st = strides or [_st(N * H * d, d, H * d)] * 4
+    arr = (sage_strides * 4)(*st)
+    if wsb is None:
+        n = ctypes.c_size_t()
+        wsb = n.value if lib.sage_workspace_bytes(B, H, N, d, ctypes.byref(n)) == 0 else 1 << 40
+    return lib.sage_attn_fwd(q, k, v, o, B, H, N, d, ctypes.c_float(sm), arr, None, ws, wsb)
+
+
+def _err(lib):
+    return lib.sage_last_error().decode()
+
+
+def test_kernel_info_and_sizes(lib):
+    from quantized_attention_diffusion_amd import _capi
+    info = _capi.sage_kernel_info()
+    assert info["arch"] == "gfx950" and info["quant_block"] == 64 and info["p_scale"] == 448.0
+    assert info["d_supported"] == [64, 128]
+    assert _capi.sage_padded_tokens(1) == 128 and _capi.sage_padded_tokens(4608) == 4608
+    assert _capi.sage_padded_tokens(32760) == 32768 and _capi.sage_padded_tokens(0) == 0
+    # the workspace holds 3 padded byte tensors plus scales and scratch
+    ws = _capi.sage_workspace_bytes(1, 24, 4608, 128)
+    assert ws >= 3 * 24 * 4608 * 128
+    assert _capi.sage_quant_scratch_bytes(1, 24, 4608, 128) < ws
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=0), -1, "q is NULL"),
+    (dict(o=0), -1, "out is NULL"),
+    (dict(d=96), -2, "head dim"),
+    (dict(N=0), -1, "must be >= 1"),
+    (dict(N=(1 << 22) + 1), -2, "SAGE_MAX_TOKENS"),
+    (dict(sm=float("nan")), -1, "sm_scale"),
+    (dict(sm=-1.0), -1, "sm_scale"),
+    (dict(q=A + 8), -3, "16-byte aligned"),
+    (dict(ws=0), -4, "workspace is NULL"),
+    (dict(ws=W + 64), -4, "256-byte aligned"),
+    (dict(wsb=1024), -4, "needed"),
+    (dict(o=A), -1, "overlaps"),
+])
+def test_fwd_rejects_bad_arguments_before_any_hip_call(lib, kw, status, msg):
+    assert _fwd(lib, **kw) == status
+    assert msg in _err(lib)
+
+
+def test_fwd_rejects_misaligned_and_overlapping_strides(lib):
+    N, H, d = 100, 2, 128
+    bad = [_st(N * H * d, d, H * d + 4)] * 4
+    assert _fwd(lib, strides=bad) == -3 and "multiples of 8" in _err(lib)
+    same_row = [_st(N * H * d, d, H * d)] * 3 + [_st(N * H * d, d, 0)]    # out rows collide
+    assert _fwd(lib, strides=same_row) == -1 and "overlap" in _err(lib)
+
+
+def test_quant_and_debug_entry_points_validate(lib):
+    from quantized_attention_diffusion_amd._capi import sage_strides
+    st = _st(100 * 2 * 64, 64, 2 * 64)
+    rc = lib.sage_quant_qk(A, B_, C, ctypes.byref(st), ctypes.byref(st), ctypes.byref(st),
+                           1, 2, 100, 64, O, O + (1 << 20), O + (2 << 20), O + (3 << 20),
+                           O + (4 << 20), O + (5 << 20), O + (6 << 20), 0, 0, None)
+    assert rc == -4 and "scratch" in _err(lib)
+    rc = lib.sage_quant_qk(A, B_, C, ctypes.byref(st), ctypes.byref(st), ctypes.byref(st),
+                           1, 2, 100, 64, O, O, O + (2 << 20), O + (3 << 20),
+                           O + (4 << 20), O + (5 << 20), O + (6 << 20), W, 1 << 20, None)
+    assert rc == -1 and "overlaps" in _err(lib)
+    rc = lib.sage_debug_qk_i32(A, B_, 1, 2, 100, 64, 0, 0, 0, 1, 2, 1, O, None)
+    assert rc == -1 and "tile range" in _err(lib)
+    rc = lib.sage_debug_qk_i32(A, B_, 1, 2, 100, 64, 0, 5, 0, 0, 1, 1, O, None)
+    assert rc == -1 and "out of range" in _err(lib)
+    assert lib.sage_debug_e4m3(A, O, -1, None) == -1
+    assert lib.sage_debug_e4m3(0, 0, 0, None) == 0          # nothing to do, no launch
+    rc = lib.sage_attn_fwd_prequant(A, A + 4096, B_, B_ + 4096, C, C + 4096, O,
+                                    ctypes.byref(st), 1, 2, 100, 64, ctypes.c_float(float("inf")), None)
+    assert rc == -1 and "sm_scale" in _err(lib)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from quantized_attention_diffusion_amd import _capi
+    monkeypatch.setattr(_capi, "_lib", None)
+    monkeypatch.setattr(_capi, "lib_path", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _capi.load()

@@ -1,0 +1,168 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI: quantised
+operands bit-exact, int32 Q.K^T tiles bit-exact, attention output within the
+max-abs bound of the oracle's quantised pipeline, on small and ragged shapes."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import quantized_attention_diffusion_amd as sage
+from gpu_helpers import (require_gpu, to_np, random_qkv, compare_quant, check_attention)
+
+pytestmark = pytest.mark.gpu
+
+KV_TILE = 128          # must equal sage_kernel_info()["kv_tile"] (checked below)
+
+CASES = [  # (B, N, H, d, seed, outliers)
+    (1, 256, 2, 64, 0, 0),      # the 'tiny' workload shape
+    (1, 1, 1, 128, 1, 0),
+    (1, 63, 3, 64, 2, 0),
+    (2, 64, 2, 128, 3, 0),
+    (1, 65, 2, 128, 4, 0),
+    (1, 127, 1, 64, 5, 0),
+    (1, 129, 2, 128, 6, 0),
+    (2, 200, 3, 128, 7, 2),
+    (1, 1000, 2, 128, 8, 4),
+    (1, 1100, 2, 64, 9, 0),     # tail of 76 keys: the last 64-key scale block is all padding
+]
+
+
+def _case_id(c):
+    return "B{}_N{}_H{}_d{}".format(*c[:4])
+
+
+def _np(t):
+    return t.float().numpy()
+
+
+def setup_module(module):
+    require_gpu()
+    info = sage.sage_kernel_info()
+    assert info["kv_tile"] == KV_TILE and info["arch"] == "gfx950"
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_quant_bit_exact(case):
+    B, N, H, d, seed, outl = case
+    print(f"[quant] {_case_id(case)}", flush=True)
+    q, k, v = random_qkv(B, N, H, d, seed, outl)
+    gq = sage.sage_quant_qk(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.quantize(_np(q), _np(k), _np(v))
+    compare_quant(gq, ref, N)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_qk_int32_tiles_bit_exact(case):
+    B, N, H, d, seed, outl = case
+    print(f"[qk_i32] {_case_id(case)}", flush=True)
+    q, k, v = random_qkv(B, N, H, d, seed, outl)
+    gq = sage.sage_quant_qk(q.cuda(), k.cuda(), v.cuda())
+    ref = oracle.quantize(_np(q), _np(k), _np(v))
+    npad = gq["q_i8"].shape[2]
+    info = sage.sage_kernel_info()
+    nqb, nkt = npad // info["block_m"], npad // info["kv_tile"]
+    for b in range(B):
+        for h in range(H):
+            s = sage.sage_debug_qk_i32(gq["q_i8"], gq["k_i8"], N, b, h, 0, 0, nqb, nkt).cpu().numpy()
+            want = oracle.qk_int32(ref["q_i8"][b, h], ref["k_i8"][b, h])        # [N, N]
+            assert np.array_equal(s[:N, :N], want), f"S differs at head ({b}, {h})"
+            assert not s[N:, :].any() and not s[:, N:].any()                    # zero padding
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_attention_matches_oracle_pipeline(case):
+    B, N, H, d, seed, outl = case
+    print(f"[attn] {_case_id(case)}", flush=True)
+    q, k, v = random_qkv(B, N, H, d, seed, outl)
+    out = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    o = to_np(out)
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE)
+    err = check_attention(o, pipe, _case_id(case))
+    exact = oracle.attention_exact(_np(q), _np(k), _np(v))
+    # the GPU adds no error beyond the specified quantisation
+    assert oracle.rel_l2(o, exact) <= oracle.rel_l2(pipe, exact) + 0.002
+    print(f"    max|gpu-pipe| = {err:.2e}  relL2(gpu, exact) = {oracle.rel_l2(o, exact):.4f}", flush=True)
+
+
+def test_tiny_workload_end_to_end():
+    w = workloads.get("tiny")
+    q, k, v = workloads.make_qkv(w)
+    out = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE)
+    check_attention(to_np(out), pipe, "tiny")
+
+
+def test_layouts_and_fused_qkv_views():
+    B, N, H, d = 1, 300, 3, 128
+    q, k, v = random_qkv(B, N, H, d, seed=21)
+    ref = to_np(sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda()))
+    # [B, H, N, d] tensors
+    qh, kh, vh = (t.transpose(1, 2).contiguous().cuda() for t in (q, k, v))
+    oh = sage.sage_attn_fwd(qh, kh, vh, layout="bhnd")
+    assert np.array_equal(to_np(oh).transpose(0, 2, 1, 3), ref)
+    # strided slices of a fused qkv projection [B, N, 3, H, d] (no copies)
+    qkv = torch.stack([q, k, v], dim=2).cuda()
+    of = sage.sage_attn_fwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2])
+    assert np.array_equal(to_np(of), ref)
+    # output written through a strided view (every other head of a wider tensor)
+    wide = torch.zeros(B, N, 2 * H, d, dtype=torch.bfloat16, device="cuda")
+    sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda(), out=wide[:, :, ::2])
+    assert np.array_equal(to_np(wide[:, :, ::2]), ref)
+    assert not wide[:, :, 1::2].any()
+
+
+def test_prequant_path_equals_fused_entry_point():
+    q, k, v = random_qkv(2, 333, 2, 128, seed=22)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    gq = sage.sage_quant_qk(qc, kc, vc)
+    a = sage.sage_attn_fwd_prequant(gq)
+    b = sage.sage_attn_fwd(qc, kc, vc)
+    assert torch.equal(a, b)
+
+
+def test_deterministic_runs():
+    q, k, v = random_qkv(1, 777, 4, 128, seed=23)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    outs = [sage.sage_attn_fwd(qc, kc, vc) for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+def test_sm_scale_argument():
+    q, k, v = random_qkv(1, 200, 2, 64, seed=24)
+    out = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda(), sm_scale=0.05)
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), sm_scale=0.05, kv_tile=KV_TILE)
+    check_attention(to_np(out), pipe, "sm_scale=0.05")
+
+
+def test_degenerate_inputs():
+    B, N, H, d = 1, 150, 2, 64
+    q, k, v = random_qkv(B, N, H, d, seed=25)
+    k[:] = k[:, :1]                      # identical keys: K' = 0, all k scales 0
+    q[:, 64:128] = 0                     # an all-zero Q block: q scale 0
+    v[:, :, :, 5] = 0                    # a zero V channel: v scale 0
+    gq = sage.sage_quant_qk(q.cuda(), k.cuda(), v.cuda())
+    ref = oracle.quantize(_np(q), _np(k), _np(v))
+    compare_quant(gq, ref, N)
+    out = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE)
+    check_attention(to_np(out), pipe, "degenerate")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_e4m3_conversion_matches_oracle_encoder():
+    t = oracle.e4m3_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2
+    base = np.concatenate([t, mids]).astype(np.float32)
+    u = base.view(np.uint32).astype(np.int64)
+    near = np.concatenate([u + dlt for dlt in range(-3, 4)])
+    near = np.clip(near, 0, None).astype(np.uint32).view(np.float32)
+    top = np.array([480.0], np.float32).view(np.uint32)[0]
+    sweep = np.arange(0, int(top) + 1, 997, dtype=np.uint32).view(np.float32)
+    x = np.concatenate([near, sweep, np.array([464.0, 470.0, 1e6, 1e-30], np.float32)])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    got = sage.sage_debug_e4m3(torch.from_numpy(x).cuda()).cpu().numpy()
+    assert np.array_equal(got, oracle.e4m3_encode(x))
