@@ -107,7 +107,7 @@ def cpu_baseline(w):
     from threadpoolctl import threadpool_limits
 
     q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
-    rows = np.linspace(0, w.N - 1, 16).astype(np.int64)
+    rows = np.linspace(0, w.N - 1, 512).astype(np.int64)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         quant = oracle.quantize(q, k, v)

@@ -31,47 +31,58 @@ namespace sage {
 
 constexpr int G = kGroupsPerWave;
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS tiles are unpadded and XOR-swizzled at 16-byte granularity so that the 16 lanes
+// served together by a 128-bit LDS read hit 16 distinct bank groups:
+//   K tile [128 keys][D bytes]:   physical chunk = chunk ^ kswz(key)
+//   V tile [D channels][128 keys]: physical chunk = chunk ^ vswz(channel)
+// (the matrix-core operand reads below touch keys 32*(r/4) + 4*kt + r%4 and channels
+// 16*dt + r for r = 0..15).
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  if constexpr (D == 128) return ((key >> 5) & 3) | (((key >> 1) & 1) << 2);
+  else return (key >> 5) & 3;
+}
+__device__ __forceinline__ int vswz(int ch) { return (ch >> 1) & 7; }
+
 template <int D>
 struct Lds {
-  static constexpr int KLD = D + 16;        // bytes per staged K row (padded)
-  static constexpr int VLD = kKvTile + 16;  // bytes per staged V channel row (padded)
-  static constexpr int KBYTES = kKvTile * KLD;
-  static constexpr int VBYTES = D * VLD;
+  static constexpr int KBYTES = kKvTile * D;   // one K tile
+  static constexpr int VBYTES = D * kKvTile;   // one V tile
+  static constexpr int STAGE = KBYTES + VBYTES;
 };
 
-// The 4 waves copy a 128 x D int8 K tile (row-major) into LDS.
+// Asynchronous copies of one K tile (128 x D int8, rows of D bytes at kg) and one V tile
+// (D channel rows of 128 e4m3 bytes at vg, row pitch npad) straight into LDS with
+// global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane i the 16 bytes
+// at offset 16*i, so the swizzle is applied by choosing which global chunk lane i reads.
+// Completion is awaited by the s_waitcnt vmcnt(0) that precedes the next barrier.
 template <int D>
-__device__ __forceinline__ void stage_k(const int8_t* __restrict__ kg, int8_t* klds) {
-  constexpr int CPR = D / 16;                 // 16-byte chunks per key row
-  constexpr int NCH = kKvTile * CPR / 256;    // chunks per thread
-  v4i buf[NCH];
+__device__ __forceinline__ void issue_k(const int8_t* __restrict__ kg, uint8_t* klds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int PW = Lds<D>::KBYTES / 1024 / kWaves;   // 1 KB blocks per wave
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    buf[i] = *(const v4i*)(kg + (c / CPR) * D + (c % CPR) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    *(v4i*)(klds + (c / CPR) * Lds<D>::KLD + (c % CPR) * 16) = buf[i];
+  for (int j = 0; j < PW; ++j) {
+    const int blk = wave * PW + j;
+    const int pos = blk * 1024 + lane * 16;
+    const int key = pos / D, pc = (pos % D) / 16;
+    const int c = pc ^ kswz<D>(key);
+    __builtin_amdgcn_global_load_lds(kg + key * D + c * 16, (lds_ptr_t)(klds + blk * 1024), 16, 0, 0);
   }
 }
 
-// The 4 waves copy a D x 128 e4m3 V tile (channel-major, row pitch npad) into LDS.
 template <int D>
-__device__ __forceinline__ void stage_v(const uint8_t* __restrict__ vg, int64_t npad, uint8_t* vlds) {
-  constexpr int CPR = kKvTile / 16;           // 8 chunks per channel row
-  constexpr int NCH = D * CPR / 256;
-  v4i buf[NCH];
+__device__ __forceinline__ void issue_v(const uint8_t* __restrict__ vg, int64_t npad, uint8_t* vlds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int PW = Lds<D>::VBYTES / 1024 / kWaves;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    buf[i] = *(const v4i*)(vg + (int64_t)(c / CPR) * npad + (c % CPR) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    *(v4i*)(vlds + (c / CPR) * Lds<D>::VLD + (c % CPR) * 16) = buf[i];
+  for (int j = 0; j < PW; ++j) {
+    const int blk = wave * PW + j;
+    const int pos = blk * 1024 + lane * 16;
+    const int ch = pos / kKvTile, pc = (pos % kKvTile) / 16;
+    const int c = pc ^ vswz(ch);
+    __builtin_amdgcn_global_load_lds(vg + (int64_t)ch * npad + c * 16, (lds_ptr_t)(vlds + blk * 1024), 16, 0, 0);
   }
 }
 
@@ -101,7 +112,7 @@ __device__ __forceinline__ void qk_tile(const int8_t* klds, const v4i (&qf)[G][D
     for (int gq = 0; gq < G; ++gq) S[gq][kt] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk) {
-      const v4i a = *(const v4i*)(klds + key * Lds<D>::KLD + 64 * kk + 16 * g);
+      const v4i a = *(const v4i*)(klds + key * D + 16 * ((4 * kk + g) ^ kswz<D>(key)));
 #pragma unroll
       for (int gq = 0; gq < G; ++gq)
         S[gq][kt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qf[gq][kk], S[gq][kt], 0, 0, 0);
@@ -110,13 +121,13 @@ __device__ __forceinline__ void qk_tile(const int8_t* klds, const v4i (&qf)[G][D
 }
 
 // Online-softmax update and P.V for one staged tile.  S is consumed: it is
-// converted to fp32 in place (|S| < 2^24, so exactly).  When `masked`, keys at tile
+// converted to fp32 in place (|S| < 2^24, so exactly).  When MASKED, keys at tile
 // index >= nvalid are removed by setting their logit to -inf; a lane whose scale
 // product is 0 then takes x = 0 and c = 1 for its valid keys, which gives the same
 // values (s = 0, p = 448 * 2^-m) without forming -inf * 0.
-template <int D>
+template <int D, bool MASKED>
 __device__ __forceinline__ void softmax_pv(v4i (&S)[G][8], const uint8_t* vlds, int lane,
-                                           float kscale, bool masked, int nvalid,
+                                           float kscale, int nvalid,
                                            const float (&qf)[G], float log2_pscale,
                                            float (&m)[G], float (&lpart)[G],
                                            v4f (&acc)[G][D / 16]) {
@@ -131,7 +142,7 @@ __device__ __forceinline__ void softmax_pv(v4i (&S)[G][8], const uint8_t* vlds, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) xf[gq][kt][i] = (float)S[gq][kt][i];
   }
-  if (masked) {
+  if constexpr (MASKED) {
     const int nv = nvalid - 32 * g;                // valid keys among this lane's 32
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
@@ -156,8 +167,7 @@ __device__ __forceinline__ void softmax_pv(v4i (&S)[G][8], const uint8_t* vlds, 
       for (int i = 0; i < 4; ++i) xm = fmaxf(xm, xf[gq][kt][i]);
     // c >= 0 and rounding is monotone, so this is the max of fp32(x * c) over the keys
     float sl = (xm == -INFINITY) ? -INFINITY : xm * c[gq];
-    sl = fmaxf(sl, __shfl_xor(sl, 16));
-    sl = fmaxf(sl, __shfl_xor(sl, 32));
+    sl = max_over_lane_groups(sl);
     const float m_new = fmaxf(m[gq], sl);
     const float nb = log2_pscale - m_new;
     const float alpha = __builtin_amdgcn_exp2f(m[gq] - m_new);
@@ -184,9 +194,10 @@ __device__ __forceinline__ void softmax_pv(v4i (&S)[G][8], const uint8_t* vlds, 
   }
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    const uint8_t* vp = vlds + (16 * dt + r) * Lds<D>::VLD + 32 * g;
-    const v4i lo = *(const v4i*)vp;
-    const v4i hi = *(const v4i*)(vp + 16);
+    const int ch = 16 * dt + r;
+    const uint8_t* vp = vlds + ch * kKvTile;
+    const v4i lo = *(const v4i*)(vp + 16 * ((2 * g) ^ vswz(ch)));
+    const v4i hi = *(const v4i*)(vp + 16 * ((2 * g + 1) ^ vswz(ch)));
     const v8i vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
     for (int gq = 0; gq < G; ++gq)
@@ -205,10 +216,21 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
 }
 
+// One key tile from an LDS stage: exact int32 S^T, then softmax and P.V.
+template <int D, bool MASKED>
+__device__ __forceinline__ void tile_step(const uint8_t* stage, const v4i (&qfr)[G][D / 64], int lane,
+                                          float ksc, int nvalid, const float (&qf)[G],
+                                          float log2_pscale, float (&m)[G], float (&lpart)[G],
+                                          v4f (&acc)[G][D / 16]) {
+  v4i S[G][8];
+  qk_tile<D>((const int8_t*)stage, qfr, lane, S);
+  softmax_pv<D, MASKED>(S, stage + Lds<D>::KBYTES, lane, ksc, nvalid, qf, log2_pscale, m, lpart, acc);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t klds[Lds<D>::KBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[Lds<D>::VBYTES];
+  // two LDS stages of (K tile, V tile): the copy of tile it+1 overlaps the compute of tile it
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Lds<D>::STAGE];
 
   const int nqb = (int)(a.npad / kBlockM);
   const int total = nqb * a.B * a.H;
@@ -219,6 +241,16 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int qrow0 = qb * kBlockM + wave * (G * 16);
   const int64_t nblk = a.npad / kQuantBlock;
+
+  const int8_t* kh = a.k_i8 + bh * a.npad * D;
+  const uint8_t* vh = a.v_f8 + bh * D * a.npad;
+  const float* ksh = a.k_scale + bh * nblk + (g >> 1);   // this lane's 64-key half of a tile
+  const int ntiles = (a.N + kKvTile - 1) / kKvTile;
+  const int tail = a.N - (ntiles - 1) * kKvTile;     // keys in the last tile (1..128)
+  const int nfull = (tail == kKvTile) ? ntiles : ntiles - 1;
+
+  issue_k<D>(kh, smem);
+  issue_v<D>(vh, a.npad, smem + Lds<D>::KBYTES);
 
   v4i qfr[G][D / 64];
   load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
@@ -232,25 +264,25 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[gq][dt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  float ksc = ksh[0];
+  __syncthreads();
 
-  const int8_t* kh = a.k_i8 + bh * a.npad * D;
-  const uint8_t* vh = a.v_f8 + bh * D * a.npad;
-  const float* ksh = a.k_scale + bh * nblk;
-  const int ntiles = (a.N + kKvTile - 1) / kKvTile;
-  const int tail = a.N - (ntiles - 1) * kKvTile;     // keys in the last tile (1..128)
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt0 = it * kKvTile;
+  for (int it = 0; it < nfull; ++it) {
+    const uint8_t* cur = smem + (it & 1) * Lds<D>::STAGE;
+    float ksc_next = 0.0f;
+    if (it + 1 < ntiles) {
+      uint8_t* nxt = smem + ((it + 1) & 1) * Lds<D>::STAGE;
+      issue_k<D>(kh + (int64_t)(it + 1) * kKvTile * D, nxt);
+      issue_v<D>(vh + (int64_t)(it + 1) * kKvTile, a.npad, nxt + Lds<D>::KBYTES);
+      ksc_next = ksh[2 * (it + 1)];
+    }
+    tile_step<D, false>(cur, qfr, lane, ksc, kKvTile, qf, a.log2_pscale, m, lpart, acc);
+    ksc = ksc_next;
     __syncthreads();
-    stage_k<D>(kh + (int64_t)kt0 * D, klds);
-    stage_v<D>(vh + kt0, a.npad, vlds);
-    __syncthreads();
-    v4i S[G][8];
-    qk_tile<D>(klds, qfr, lane, S);
-    const float ksc = ksh[(kt0 + 64 * (g >> 1)) / kQuantBlock];
-    const bool masked = (it == ntiles - 1) && (tail != kKvTile);
-    softmax_pv<D>(S, vlds, lane, ksc, masked, tail, qf, a.log2_pscale, m, lpart, acc);
   }
+  if (nfull < ntiles)   // last tile with keys beyond N: already staged in stage nfull & 1
+    tile_step<D, true>(smem + (nfull & 1) * Lds<D>::STAGE, qfr, lane, ksc, tail, qf,
+                       a.log2_pscale, m, lpart, acc);
 
   // epilogue: total row sum over the 4 lanes of each query, normalise, V scale, bf16
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
@@ -258,8 +290,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const float* vsh = a.v_scale + bh * D;
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
-    float l = lpart[gq] + __shfl_xor(lpart[gq], 16);
-    l = l + __shfl_xor(l, 32);
+    const float l = sum_over_lane_groups(lpart[gq]);
     const float rl = 1.0f / l;
     const int qrow = qrow0 + 16 * gq + r;
     if (qrow < a.N) {
@@ -283,17 +314,17 @@ __global__ __launch_bounds__(256) void k_debug_qk(const int8_t* __restrict__ q_i
                                                   const int8_t* __restrict__ k_i8, int64_t npad,
                                                   int64_t bh, int q_block, int kv_tile,
                                                   int n_kv_tiles, int32_t* __restrict__ s_out) {
-  __shared__ __attribute__((aligned(16))) int8_t klds[Lds<D>::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t klds[Lds<D>::KBYTES];
   const int qb = q_block + blockIdx.y, kvt = kv_tile + blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int qrow0 = qb * kBlockM + wave * (G * 16);
+  issue_k<D>(k_i8 + bh * npad * D + (int64_t)kvt * kKvTile * D, klds);
   v4i qfr[G][D / 64];
   load_q<D>(q_i8 + bh * npad * D, qrow0, lane, qfr);
-  stage_k<D>(k_i8 + bh * npad * D + (int64_t)kvt * kKvTile * D, klds);
   __syncthreads();
   v4i S[G][8];
-  qk_tile<D>(klds, qfr, lane, S);
+  qk_tile<D>((const int8_t*)klds, qfr, lane, S);
   const int64_t ld = (int64_t)n_kv_tiles * kKvTile;
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
