@@ -17,7 +17,7 @@ SOURCES = ["sage_api.hip", "sage_quant.hip", "sage_attn.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for all device code.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
+FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 
