@@ -10,8 +10,11 @@ constexpr int kQuantBlock = 64;     // tokens per Q/K scale block
 constexpr int kTokenAlign = 128;    // Npad alignment (one key tile)
 constexpr int kKvTile = 128;        // keys per online-softmax step
 constexpr int kWaves = 4;           // waves per attention workgroup
+constexpr int kThreads = kWaves * 64;
 constexpr int kGroupsPerWave = 2;   // 16-query groups per wave
-constexpr int kBlockM = kWaves * kGroupsPerWave * 16;   // 128 query rows per workgroup
+constexpr int kBlockM = kWaves * kGroupsPerWave * 16;   // query rows per workgroup
+constexpr int kStages = 2;          // LDS stages (K tile + V tile) of the attention kernel
+constexpr int kMinWavesPerSimd = 2; // occupancy the attention kernel is compiled for
 constexpr float kPScale = 448.0f;   // static scale of P before e4m3 rounding
 constexpr int kStatsChunk = 256;    // tokens per partial-sum chunk of the quantisation pass
 
