@@ -16,14 +16,24 @@ constexpr int kBlockM = kWaves * kGroupsPerWave * 16;   // query rows per workgr
 constexpr int kStages = 2;          // LDS stages (K tile + V tile) of the attention kernel
 constexpr int kMinWavesPerSimd = 2; // occupancy the attention kernel is compiled for
 constexpr float kPScale = 448.0f;   // static scale of P before e4m3 rounding
-constexpr int kStatsChunk = 256;    // tokens per partial-sum chunk of the quantisation pass
+constexpr int kMaxStatsChunks = 128; // partial-statistics rows per (b, h) in the quantisation pass
 
 struct Strides { int64_t b, h, n; };
 
 inline int64_t padded_tokens(int n) {
   return n <= 0 ? 0 : ((int64_t)n + kTokenAlign - 1) / kTokenAlign * kTokenAlign;
 }
-inline int stats_chunks(int n) { return (n + kStatsChunk - 1) / kStatsChunk; }
+// 64-token blocks per first-pass workgroup: the fewest that keep the number of partial
+// rows per (b, h) within kMaxStatsChunks.
+inline int stats_blocks_per_chunk(int64_t npad) {
+  const int64_t nblk = npad / kQuantBlock;
+  return (int)((nblk + kMaxStatsChunks - 1) / kMaxStatsChunks);
+}
+inline int stats_chunks(int n) {
+  const int64_t nblk = padded_tokens(n) / kQuantBlock;
+  const int per = stats_blocks_per_chunk(padded_tokens(n));
+  return (int)((nblk + per - 1) / per);
+}
 
 // Operands of the quantisation pass.
 struct QuantArgs {

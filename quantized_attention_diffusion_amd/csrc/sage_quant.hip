@@ -4,80 +4,24 @@
 // ComfyUI-sol-attn page, "核心亮点" item 1).
 //
 // Three launches, all HBM-bound:
-//   1. stats    grid (chunks of 256 tokens, H, B): fp64 partial sums of K and partial
-//               max |V| per channel, read with 16-byte loads along the channel axis.
-//   2. finalize grid (B*H): sums the partials in chunk order -> k_mean (bf16),
-//               v_scale = vamax/448 and 448/vamax.
-//   3. codes    grid (Npad/64, H, B): one 64-token block of Q, K and V per workgroup;
-//               block max-abs reduced across the workgroup, codes written with 8-byte
-//               stores; V codes are transposed through LDS into the channel-major
-//               layout the attention kernel stages directly.
+//   1. q+stats  grid (chunks, H, B): each workgroup walks a run of 64-token blocks; it
+//               writes the final INT8 codes and scales of Q (they need only the block
+//               itself) and one row of fp64 partial sums of K and partial max |V| per
+//               channel.  The run length grows with N so a head never has more than
+//               kMaxStatsChunks partial rows.
+//   2. finalize grid (B*H): sums the partial rows -> k_mean (bf16), v_scale =
+//               vamax/448 and 448/vamax.
+//   3. k+v      grid (Npad/64, H, B): one 64-token block of K and V per workgroup
+//               (both read again, usually from the last-level cache); block max-abs
+//               reduced across the workgroup, K codes written with 8-byte stores; V
+//               codes transposed through LDS into the channel-major layout the
+//               attention kernel stages directly.
+// Every workgroup issues all of its row loads before the first reduction, so each
+// thread keeps 8 to 12 16-byte loads in flight.
 #include "sage_internal.h"
 #include "sage_device.h"
 
 namespace sage {
-
-template <int D>
-__global__ __launch_bounds__(256) void k_quant_stats(
-    const uint16_t* __restrict__ k, Strides sk, const uint16_t* __restrict__ v, Strides sv,
-    int H, int N, int chunks, double* __restrict__ ksum_part, float* __restrict__ vmax_part) {
-  constexpr int TPR = D / 8;        // threads per token row, 8 channels each
-  constexpr int RPI = 256 / TPR;    // token rows per iteration
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, r = t / TPR, cg = t % TPR;
-  const int n0 = chunk * kStatsChunk;
-  const int n1 = min(N, n0 + kStatsChunk);
-  const uint16_t* kb = k + (int64_t)b * sk.b + (int64_t)h * sk.h + 8 * cg;
-  const uint16_t* vb = v + (int64_t)b * sv.b + (int64_t)h * sv.h + 8 * cg;
-  double s[8];
-  float vm[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) { s[j] = 0.0; vm[j] = 0.0f; }
-#pragma unroll 4
-  for (int n = n0 + r; n < n1; n += RPI) {
-    const uint4 kw = *(const uint4*)(kb + (int64_t)n * sk.n);
-    const uint4 vw = *(const uint4*)(vb + (int64_t)n * sv.n);
-    float kx[8], vx[8];
-    bf16x8_to_f32(kw, kx);
-    bf16x8_to_f32(vw, vx);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s[j] += (double)kx[j];
-      vm[j] = fmaxf(vm[j], fabsf(vx[j]));
-    }
-  }
-  __shared__ __attribute__((aligned(16))) double red_s[RPI][D];
-  __shared__ float red_v[RPI][D];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) { red_s[r][8 * cg + j] = s[j]; red_v[r][8 * cg + j] = vm[j]; }
-  __syncthreads();
-  if (t < D) {
-    double acc = 0.0;
-    float m = 0.0f;
-    for (int i = 0; i < RPI; ++i) { acc += red_s[i][t]; m = fmaxf(m, red_v[i][t]); }
-    const int64_t o = ((int64_t)(b * H + h) * chunks + chunk) * D + t;
-    ksum_part[o] = acc;
-    vmax_part[o] = m;
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(D) void k_quant_finalize(
-    const double* __restrict__ ksum_part, const float* __restrict__ vmax_part, int chunks, int N,
-    uint16_t* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
-  const int64_t bh = blockIdx.x;
-  const int c = threadIdx.x;
-  double s = 0.0;
-  float vm = 0.0f;
-  for (int i = 0; i < chunks; ++i) {
-    s += ksum_part[(bh * chunks + i) * D + c];
-    vm = fmaxf(vm, vmax_part[(bh * chunks + i) * D + c]);
-  }
-  const float mean = (float)(s / (double)N);        // fp64 divide, one rounding to fp32
-  k_mean[bh * D + c] = (uint16_t)f32_to_bf16_rne(mean);
-  v_scale[bh * D + c] = vm / kPScale;               // IEEE division (0 when vm = 0)
-  v_inv[bh * D + c] = vm > 0.0f ? kPScale / vm : 0.0f;
-}
 
 // INT8 codes of one 64-token block held as x[RPT][8] per thread; returns the scale.
 template <int RPT>
@@ -103,99 +47,197 @@ __device__ __forceinline__ float int8_block(const float (&x)[RPT][8], uint2 (&co
   return amax / 127.0f;
 }
 
+// Loads the 16-byte words (8 channels) of rows row0 + r + RPI*i of one 64-token block;
+// rows at or past N read as zero.
+template <int RPT, int RPI>
+__device__ __forceinline__ void load_block(const uint16_t* base, int64_t stride_n, int row0, int r,
+                                           int N, uint4 (&w)[RPT]) {
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int n = row0 + r + RPI * i;
+    w[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N) w[i] = *(const uint4*)(base + (int64_t)n * stride_n);
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_quant_codes(
+__global__ __launch_bounds__(256) void k_quant_q_stats(
     const uint16_t* __restrict__ q, Strides sq, const uint16_t* __restrict__ k, Strides sk,
-    const uint16_t* __restrict__ v, Strides sv, int H, int N, int64_t npad,
-    const uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
-    int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int8_t* __restrict__ k_i8,
-    float* __restrict__ k_scale, uint8_t* __restrict__ v_f8) {
+    const uint16_t* __restrict__ v, Strides sv, int H, int N, int64_t npad, int blocks_per_chunk,
+    int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
+    double* __restrict__ ksum_part, float* __restrict__ vmax_part) {
+  constexpr int TPR = D / 8;        // threads per token row, 8 channels each
+  constexpr int RPI = 256 / TPR;    // token rows per sweep of the workgroup
+  constexpr int RPT = kQuantBlock / RPI;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, r = t / TPR, cg = t % TPR;
+  const int64_t bh = (int64_t)b * gridDim.y + h;
+  const int64_t nblk = npad / kQuantBlock;
+  const int blk0 = chunk * blocks_per_chunk;
+  const int blk1 = (int)min((int64_t)blk0 + blocks_per_chunk, nblk);
+  const uint16_t* qb = q + (int64_t)b * sq.b + (int64_t)h * sq.h + 8 * cg;
+  const uint16_t* kb = k + (int64_t)b * sk.b + (int64_t)h * sk.h + 8 * cg;
+  const uint16_t* vb = v + (int64_t)b * sv.b + (int64_t)h * sv.h + 8 * cg;
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) double red_s[RPI][D];
+  __shared__ float red_v[RPI][D];
+
+  double s[8];
+  float vm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { s[j] = 0.0; vm[j] = 0.0f; }
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int row0 = blk * kQuantBlock;
+    uint4 qw[RPT], kw[RPT], vw[RPT];
+    load_block<RPT, RPI>(qb, sq.n, row0, r, N, qw);
+    load_block<RPT, RPI>(kb, sk.n, row0, r, N, kw);
+    load_block<RPT, RPI>(vb, sv.n, row0, r, N, vw);
+    float x[RPT][8];
+    uint2 codes[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) bf16x8_to_f32(qw[i], x[i]);
+    const float scale = int8_block<RPT>(x, codes, red);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      *(uint2*)(q_i8 + (bh * npad + row0 + r + RPI * i) * D + 8 * cg) = codes[i];
+    if (t == 0) q_scale[bh * nblk + blk] = scale;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float kx[8], vx[8];
+      bf16x8_to_f32(kw[i], kx);
+      bf16x8_to_f32(vw[i], vx);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s[j] += (double)kx[j];
+        vm[j] = fmaxf(vm[j], fabsf(vx[j]));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { red_s[r][8 * cg + j] = s[j]; red_v[r][8 * cg + j] = vm[j]; }
+  __syncthreads();
+  if (t < D) {
+    double acc = 0.0;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPI; ++i) { acc += red_s[i][t]; m = fmaxf(m, red_v[i][t]); }
+    const int64_t o = (bh * gridDim.x + chunk) * D + t;
+    ksum_part[o] = acc;
+    vmax_part[o] = m;
+  }
+}
+
+// One workgroup per (b, h): 1024 threads = D channels x (1024 / D) slices of the
+// partial rows, combined through LDS in slice order.
+constexpr int kFinalizeThreads = 1024;
+template <int D>
+__global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
+    const double* __restrict__ ksum_part, const float* __restrict__ vmax_part, int chunks, int N,
+    uint16_t* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
+  constexpr int SL = kFinalizeThreads / D;
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x % D, sl = threadIdx.x / D;
+  __shared__ double ps[SL][D];
+  __shared__ float pv[SL][D];
+  double s = 0.0;
+  float vm = 0.0f;
+#pragma unroll 4
+  for (int i = sl; i < chunks; i += SL) {
+    s += ksum_part[(bh * chunks + i) * D + c];
+    vm = fmaxf(vm, vmax_part[(bh * chunks + i) * D + c]);
+  }
+  ps[sl][c] = s;
+  pv[sl][c] = vm;
+  __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int i = 1; i < SL; ++i) { s += ps[i][c]; vm = fmaxf(vm, pv[i][c]); }
+    const float mean = (float)(s / (double)N);        // fp64 divide, one rounding to fp32
+    k_mean[bh * D + c] = (uint16_t)f32_to_bf16_rne(mean);
+    v_scale[bh * D + c] = vm / kPScale;               // IEEE division (0 when vm = 0)
+    v_inv[bh * D + c] = vm > 0.0f ? kPScale / vm : 0.0f;
+  }
+}
+
+// K - mean codes and V codes of one 64-token block.  Here thread (r, cg) holds the RPT
+// consecutive tokens RPT*r .. RPT*r + RPT-1 (8 channels each), so for every channel it
+// owns RPT adjacent bytes of the channel-major V block: they go to LDS as one word
+// (RPT = 4) or half word (RPT = 2), in rows of VW words whose odd pitch spreads the
+// 16 channel groups of a wave over distinct banks (at most 2 lanes per bank).
+template <int D>
+__global__ __launch_bounds__(256) void k_quant_kv(
+    const uint16_t* __restrict__ k, Strides sk, const uint16_t* __restrict__ v, Strides sv,
+    int H, int N, int64_t npad, const uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_f8) {
   constexpr int TPR = D / 8;
   constexpr int RPI = 256 / TPR;
-  constexpr int RPT = kQuantBlock / RPI;   // token rows per thread
-  constexpr int VLD = kQuantBlock + 16;    // LDS row pitch of the transposed V block
+  constexpr int RPT = kQuantBlock / RPI;   // consecutive tokens per thread (4 or 2)
+  constexpr int VW = kQuantBlock / 4 + 1;  // LDS words per channel row (odd pitch)
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, r = t / TPR, cg = t % TPR;
   const int64_t bh = (int64_t)b * gridDim.y + h;
   const int row0 = blk * kQuantBlock;
+  const int tok0 = row0 + RPT * r;           // this thread's first token
   const int64_t nblk = npad / kQuantBlock;
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[D][VLD];
+  __shared__ uint32_t vt[D * VW];
 
-  float x[RPT][8];
-  uint2 codes[RPT];
+  uint4 kw[RPT], vw[RPT];
+  load_block<RPT, 1>(k + (int64_t)b * sk.b + (int64_t)h * sk.h + 8 * cg, sk.n, tok0, 0, N, kw);
+  load_block<RPT, 1>(v + (int64_t)b * sv.b + (int64_t)h * sv.h + 8 * cg, sv.n, tok0, 0, N, vw);
+  float mu[8], inv[8];
+  bf16x8_to_f32(*(const uint4*)(k_mean + bh * D + 8 * cg), mu);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) inv[j] = v_inv[bh * D + 8 * cg + j];
 
-  // ---- Q ----
+  // ---- K - mean -> INT8 ----
   {
-    const uint16_t* base = q + (int64_t)b * sq.b + (int64_t)h * sq.h + 8 * cg;
+    float x[RPT][8];
+    uint2 codes[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int n = row0 + r + RPI * i;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (n < N) w = *(const uint4*)(base + (int64_t)n * sq.n);
-      bf16x8_to_f32(w, x[i]);
+      const bool valid = tok0 + i < N;
+      bf16x8_to_f32(kw[i], x[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[i][j] = valid ? x[i][j] - mu[j] : 0.0f;
     }
     const float scale = int8_block<RPT>(x, codes, red);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int n = row0 + r + RPI * i;
-      *(uint2*)(q_i8 + (bh * npad + n) * D + 8 * cg) = codes[i];
-    }
-    if (t == 0) q_scale[bh * nblk + blk] = scale;
-  }
-  // ---- K - mean ----
-  {
-    float mu[8];
-    const uint4 mw = *(const uint4*)(k_mean + bh * D + 8 * cg);
-    bf16x8_to_f32(mw, mu);
-    const uint16_t* base = k + (int64_t)b * sk.b + (int64_t)h * sk.h + 8 * cg;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int n = row0 + r + RPI * i;
-      if (n < N) {
-        const uint4 w = *(const uint4*)(base + (int64_t)n * sk.n);
-        bf16x8_to_f32(w, x[i]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[i][j] = x[i][j] - mu[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
-      }
-    }
-    const float scale = int8_block<RPT>(x, codes, red);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int n = row0 + r + RPI * i;
-      *(uint2*)(k_i8 + (bh * npad + n) * D + 8 * cg) = codes[i];
-    }
+    for (int i = 0; i < RPT; ++i)
+      *(uint2*)(k_i8 + (bh * npad + tok0 + i) * D + 8 * cg) = codes[i];
     if (t == 0) k_scale[bh * nblk + blk] = scale;
   }
   // ---- V -> e4m3, transposed to [channel][token] ----
   {
-    float inv[8];
+    uint32_t packed[8];                    // channel j: codes of tokens tok0 .. tok0+RPT-1
 #pragma unroll
-    for (int j = 0; j < 8; ++j) inv[j] = v_inv[bh * D + 8 * cg + j];
-    const uint16_t* base = v + (int64_t)b * sv.b + (int64_t)h * sv.h + 8 * cg;
+    for (int j = 0; j < 8; ++j) packed[j] = 0u;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int n = row0 + r + RPI * i;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (n < N) w = *(const uint4*)(base + (int64_t)n * sv.n);
-      bf16x8_to_f32(w, x[i]);
+      float x[8];
+      bf16x8_to_f32(vw[i], x);
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const uint32_t c2 = e4m3x2_sat(x[i][j] * inv[j], x[i][j + 1] * inv[j + 1]);
-        vt[8 * cg + j][r + RPI * i] = (uint8_t)(c2 & 0xff);
-        vt[8 * cg + j + 1][r + RPI * i] = (uint8_t)(c2 >> 8);
+        const uint32_t c2 = e4m3x2_sat(x[j] * inv[j], x[j + 1] * inv[j + 1]);
+        packed[j] |= (c2 & 0xffu) << (8 * i);
+        packed[j + 1] |= (c2 >> 8) << (8 * i);
       }
+    }
+    if constexpr (RPT == 4) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vt[(8 * cg + j) * VW + r] = packed[j];
+    } else {
+      uint16_t* vt16 = (uint16_t*)vt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vt16[(8 * cg + j) * 2 * VW + r] = (uint16_t)packed[j];
     }
     __syncthreads();
     constexpr int NCH = D * (kQuantBlock / 16);      // 16-byte chunks of the block
 #pragma unroll
     for (int cid = t; cid < NCH; cid += 256) {
       const int c = cid / (kQuantBlock / 16), part = cid % (kQuantBlock / 16);
-      const uint4 w = *(const uint4*)(&vt[c][16 * part]);
-      *(uint4*)(v_f8 + (bh * D + c) * npad + row0 + 16 * part) = w;
+      const uint32_t* src = vt + c * VW + 4 * part;
+      *(uint4*)(v_f8 + (bh * D + c) * npad + row0 + 16 * part) = make_uint4(src[0], src[1], src[2], src[3]);
     }
   }
 }
@@ -214,14 +256,16 @@ __global__ void k_debug_e4m3(const float* __restrict__ x, uint8_t* __restrict__ 
 
 template <int D>
 static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
+  const int per = stats_blocks_per_chunk(a.npad);
   const int chunks = stats_chunks(a.N);
-  hipLaunchKernelGGL(k_quant_stats<D>, dim3(chunks, a.H, a.B), dim3(256), 0, s,
-                     a.k, a.sk, a.v, a.sv, a.H, a.N, chunks, a.ksum_part, a.vmax_part);
-  hipLaunchKernelGGL(k_quant_finalize<D>, dim3(a.B * a.H), dim3(D), 0, s,
+  hipLaunchKernelGGL(k_quant_q_stats<D>, dim3(chunks, a.H, a.B), dim3(256), 0, s,
+                     a.q, a.sq, a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, per,
+                     a.q_i8, a.q_scale, a.ksum_part, a.vmax_part);
+  hipLaunchKernelGGL(k_quant_finalize<D>, dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
                      a.ksum_part, a.vmax_part, chunks, a.N, a.k_mean, a.v_scale, a.v_inv);
-  hipLaunchKernelGGL(k_quant_codes<D>, dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
-                     a.q, a.sq, a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, a.k_mean, a.v_inv,
-                     a.q_i8, a.q_scale, a.k_i8, a.k_scale, a.v_f8);
+  hipLaunchKernelGGL(k_quant_kv<D>, dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
+                     a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, a.k_mean, a.v_inv,
+                     a.k_i8, a.k_scale, a.v_f8);
   return hipGetLastError();
 }
 
