@@ -7,7 +7,7 @@ kernel's matrix-core roofline fraction, the quantisation pass's HBM rate, the sa
 figures at N=16384 and N=65536, and the CPU oracle timed on a bounded sample.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
-                [--no-cpu-baseline]
+                [--no-cpu-baseline] [--pmc-run]
 """
 from __future__ import annotations
 
@@ -23,6 +23,10 @@ sys.path.insert(0, ROOT)
 PEAK_TOPS = 5000.0        # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s), x1000
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 SWEEP = ["sweep16k", "stress"]
+COPY_BYTES = 1 << 30      # calibration copy of the counter runs
+ATTN_SOURCES = ["quantized_attention_diffusion_amd/csrc/sage_attn.hip",
+                "quantized_attention_diffusion_amd/csrc/sage_device.h",
+                "quantized_attention_diffusion_amd/csrc/sage_internal.h"]
 
 
 def _parse():
@@ -33,6 +37,8 @@ def _parse():
     ap.add_argument("--workload", default="flux_like")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="only run the short program that the rocprofv3 counter runs profile")
     return ap.parse_args()
 
 
@@ -97,28 +103,114 @@ def measure(w, steps, warmup):
                 quant_gbs=quant_bytes(w) / (quant_ms * 1e-3) / 1e9)
 
 
-def cpu_baseline(w):
-    """The CPU oracle (numpy) on a bounded sample of the workload: the full
-    quantisation of Q, K and V, plus the quantised attention of a sample of query rows
-    in every head; scaled to the whole workload linearly in rows."""
+def _oracle_rows_worker(args):
+    """One worker of the CPU baseline: rebuilds the seeded inputs and their oracle
+    quantisation (untimed set-up), then times the oracle's quantised attention of its
+    share of the sampled query rows in every head."""
+    name, rows = args
     import numpy as np
     import oracle
     import workloads
     from threadpoolctl import threadpool_limits
 
+    w = workloads.get(name)
+    with threadpool_limits(limits=1):
+        q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+        quant = oracle.quantize(q, k, v)
+        t0 = time.perf_counter()
+        oracle.attention_pipeline(q, k, v, kv_tile=128, rows=np.asarray(rows), quant=quant)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, rows_total: int = 1536):
+    """The CPU oracle (numpy) on a bounded sample of the workload: the full
+    quantisation of Q, K and V on one core, then the quantised attention of
+    ``rows_total`` query rows in every head, split over one worker process per host
+    core (up to 16), each with one BLAS thread.  Scaled to the whole workload
+    linearly in rows (rows are independent given the quantised K and V)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
     q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
-    rows = np.linspace(0, w.N - 1, 512).astype(np.int64)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        quant = oracle.quantize(q, k, v)
-        t1 = time.perf_counter()
-        oracle.attention_pipeline(q, k, v, kv_tile=128, rows=rows, quant=quant)
-        t2 = time.perf_counter()
-    est = (t1 - t0) + (t2 - t1) * w.N / len(rows)
-    return {"value": round(w.ops / est / 1e12, 8), "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": (f"{w.name}: full quantisation ({t1 - t0:.1f} s) + attention of "
-                       f"{len(rows)} of {w.N} query rows in all {w.H} heads ({t2 - t1:.1f} s), "
-                       f"scaled by rows to {est:.0f} s per step; numpy, 1 thread")}
+        oracle.quantize(q, k, v)
+        t_quant = time.perf_counter() - t0
+    del q, k, v
+    rows = np.linspace(0, w.N - 1, rows_total).astype(np.int64)
+    shares = [rows[i::cores].tolist() for i in range(cores)]
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        times = list(ex.map(_oracle_rows_worker, [(w.name, s) for s in shares]))
+    t_rows = max(times)                      # the workers run concurrently
+    est = t_quant + t_rows * w.N / rows_total
+    return {"value": round(w.ops / est / 1e12, 8), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": (f"{w.name}: full quantisation on 1 core ({t_quant:.1f} s), then attention of "
+                       f"{rows_total} of {w.N} query rows in all {w.H} heads split over {cores} "
+                       f"processes ({t_rows:.1f} s wall, {sum(times):.1f} s CPU); scaled by rows "
+                       f"to {est:.0f} s per step; numpy, 1 BLAS thread per process")}
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources that define the attention kernel; a recorded traffic
+    figure is used only while it matches."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a device
+    copy of known size), or None when there is none for this workload or the kernel
+    source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("source_hash") == kernel_source_hash():
+                    return rec
+    return None
+
+
+def pmc_run(w, reps: int = 3):
+    """Short program for rocprofv3 counter runs: a 1 GiB elementwise copy kernel
+    (calibrates the byte counters against a known size), then ``reps`` quantisation
+    passes and ``reps`` attention launches on the workload."""
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)        # an elementwise kernel: reads and writes COPY_BYTES
+    torch.cuda.synchronize(dev)
+    q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
+    quant = sage.sage_quant_qk(q, k, v)
+    out = torch.empty_like(q)
+    for _ in range(reps):
+        sage.sage_quant_qk(q, k, v, out=quant)
+    torch.cuda.synchronize(dev)
+    for _ in range(reps):
+        sage.sage_attn_fwd_prequant(quant, out=out)
+    torch.cuda.synchronize(dev)
+    print(f"[bench] pmc run done: copy {COPY_BYTES} B x{reps}, quant x{reps}, attention x{reps}",
+          file=sys.stderr, flush=True)
 
 
 def main():
@@ -127,15 +219,27 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); heads would be "
               "sharded across GPUs with no communication, see the design notes.", file=sys.stderr)
         sys.exit(2)
-    import torch
     import workloads
+
+    w = workloads.get(args.workload)
+    # The CPU baseline runs first, in worker processes started before this process
+    # touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline and not args.pmc_run:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+        print(f"[bench] cpu baseline done: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    import torch
     import quantized_attention_diffusion_amd as sage
 
     sage.load()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    w = workloads.get(args.workload)
+    if args.pmc_run:
+        pmc_run(w)
+        return
     print(f"[bench] {w.name} B={w.B} H={w.H} N={w.N} d={w.d}: {args.warmup} warmup + {args.steps} steps",
           file=sys.stderr, flush=True)
     r = measure(w, args.steps, args.warmup)
@@ -151,11 +255,8 @@ def main():
                            "mfma_util": round(rs["attn_tops"] / PEAK_TOPS, 4),
                            "quant_ms": round(rs["quant_ms"], 4),
                            "quant_gbs": round(rs["quant_gbs"], 1)}
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w)
     info = sage.sage_kernel_info()
+    traffic = recorded_traffic(w.name)
     line = {
         "metric": "quantized-attention TOPS (4*B*H*N^2*d per step: quantisation + attention)",
         "value": round(r["tops"], 3),
@@ -177,7 +278,9 @@ def main():
                        "hbm_frac": round(r["quant_gbs"] / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(r["attn_tops"] / PEAK_TOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "kernel": "k_attn<%d>" % w.d,
+                     "algorithmic_bytes": 5 * w.B * w.H * w.N * w.d},
         "sweep": sweep,
         "cpu_baseline": cpu,
     }

@@ -1,0 +1,86 @@
+"""GPU parity at the benchmark's full sizes, through the C ABI, in the launch
+configuration the bench times (one sage_attn_fwd over the whole workload).
+
+The oracle cannot evaluate every output at these sizes, so each test checks samples it
+can compute one by one:
+
+- quantised operands of three heads, bit-exact: every scale, the K mean, all V codes,
+  and sampled 64-token blocks of Q and K codes;
+- int32 S tiles at sampled (query block, key tile) positions, including the last,
+  ragged key tile;
+- the attention output of sampled query rows of those heads against the oracle's
+  quantised pipeline (rows are independent given the quantised K and V), plus
+  rel-L2 against fp64 exact attention on the same rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import quantized_attention_diffusion_amd as sage
+from gpu_helpers import require_gpu, to_np, compare_quant, check_attention
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["flux_like", "sweep8k", "sweep16k", "video", "stress"]
+N_ROWS = 40          # sampled query rows per head
+N_BLOCKS = 12        # sampled 64-token Q/K code blocks per head
+N_TILES = 3          # sampled S tiles per head
+
+
+def setup_module(module):
+    require_gpu()
+
+
+def _head(t, h):
+    """[B, N, H, d] bf16 CPU tensor -> float32 numpy [B, N, 1, d] of head h."""
+    return t[:, :, h:h + 1, :].float().numpy()
+
+
+def _head_quant(gq, h):
+    return {key: (val[:, h:h + 1] if isinstance(val, torch.Tensor) else val) for key, val in gq.items()}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_parity(name):
+    w = workloads.get(name)
+    print(f"[full] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
+    q, k, v = workloads.make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = sage.sage_attn_fwd(qd, kd, vd)
+    gq = sage.sage_quant_qk(qd, kd, vd)
+    torch.cuda.synchronize()
+    info = sage.sage_kernel_info()
+    N, T, bm = w.N, info["kv_tile"], info["block_m"]
+    npad = sage.sage_padded_tokens(N)
+    rng = np.random.default_rng(1234)
+    heads = sorted({0, w.H - 1, int(rng.integers(1, w.H - 1))})
+    nb = -(-N // 64)
+    for h in heads:
+        qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
+        ref = oracle.quantize(qh, kh, vh)
+        # quantised operands
+        blocks = sorted({0, nb - 1, *rng.choice(nb, size=N_BLOCKS - 2, replace=False).tolist()})
+        compare_quant(_head_quant(gq, h), ref, N, blocks=blocks)
+        # int32 S tiles (query block, key tile), the last key tile always included
+        nqb, nkt = npad // bm, npad // T
+        tiles = [(int(rng.integers(nqb)), nkt - 1)] + \
+                [(int(rng.integers(nqb)), int(rng.integers(nkt))) for _ in range(N_TILES - 1)]
+        for qb, kt in tiles:
+            s = sage.sage_debug_qk_i32(gq["q_i8"], gq["k_i8"], N, 0, h, qb, kt).cpu().numpy()
+            r0, c0 = qb * bm, kt * T
+            r1, c1 = min(N, r0 + bm), min(N, c0 + T)
+            want = oracle.qk_int32(ref["q_i8"][0, 0, r0:r1], ref["k_i8"][0, 0, c0:c1])
+            assert np.array_equal(s[:r1 - r0, :c1 - c0], want), f"{name} head {h}: S tile {(qb, kt)} differs"
+            assert not s[r1 - r0:, :].any() and not s[:, c1 - c0:].any()
+        # attention output of sampled rows
+        rows = np.unique(np.concatenate([[0, N - 1], np.arange(max(0, N - 5), N),
+                                         rng.choice(N, size=N_ROWS, replace=False)]))
+        pipe = oracle.attention_pipeline(qh, kh, vh, kv_tile=T, rows=rows, quant=ref)
+        o = to_np(out[:, rows, h:h + 1, :])
+        err = check_attention(o, pipe, f"{name} head {h}")
+        exact = oracle.attention_exact(qh, kh, vh, rows=rows)
+        r_gpu, r_pipe = oracle.rel_l2(o, exact), oracle.rel_l2(pipe, exact)
+        print(f"    head {h}: max|gpu-pipe| = {err:.2e}  relL2 gpu {r_gpu:.4f}  pipe {r_pipe:.4f}", flush=True)
+        assert r_gpu <= r_pipe + 0.002
