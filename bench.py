@@ -122,7 +122,7 @@ def _oracle_rows_worker(args):
         return time.perf_counter() - t0
 
 
-def cpu_baseline(w, rows_total: int = 1536):
+def cpu_baseline(w, rows_total: int = 3072):
     """The CPU oracle (numpy) on a bounded sample of the workload: the full
     quantisation of Q, K and V on one core, then the quantised attention of
     ``rows_total`` query rows in every head, split over one worker process per host
@@ -143,6 +143,7 @@ def cpu_baseline(w, rows_total: int = 1536):
         oracle.quantize(q, k, v)
         t_quant = time.perf_counter() - t0
     del q, k, v
+    rows_total = min(rows_total, w.N)
     rows = np.linspace(0, w.N - 1, rows_total).astype(np.int64)
     shares = [rows[i::cores].tolist() for i in range(cores)]
     ctx = mp.get_context("spawn")

@@ -34,6 +34,16 @@ Readings (the pages give none of these details):
   sum_j p8_ij * v8_j; O = acc * v_scale / l.  (The 448 cancels between acc and l.)
   acc and l are kept in fp64 here; they decide no code.
 * Keys at or beyond N do not exist (no padding in the oracle).
+
+Quality mode (``bf16_p=True, fp8_p=False, fp8_v=False``): the pages mention that
+quantised attention schemes offer a quality-first setting next to the speed-first one
+(bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 4.3) and that
+critical work should keep 16-bit attention for P.V (apatero page
+"TeaCache和SageAttention优化实现更快的AI图像生成", section on when quality differences
+appear).  Reading: Q.K^T stays INT8 exactly as above; the same fp32 p (including the
+static 448) is rounded to bf16 (nearest, ties to even) instead of e4m3; V is not
+quantised (its bf16 values are used as they are, scale 1); l still accumulates the
+unrounded p.
 """
 from __future__ import annotations
 
@@ -42,7 +52,7 @@ import math
 import numpy as np
 
 from .fp8 import e4m3_encode, e4m3_decode
-from .quant import quantize, QUANT_BLOCK
+from .quant import quantize, QUANT_BLOCK, bf16_round
 
 __all__ = ["LOG2E", "default_sm_scale", "attention_exact", "qk_int32",
            "attention_pipeline", "rel_l2"]
@@ -107,14 +117,19 @@ def _exp2_f32(x):
 
 def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                        quant=None, int8_qk: bool = True, fp8_p: bool = True,
-                       fp8_v: bool = True, smooth_k: bool = True) -> np.ndarray:
+                       fp8_v: bool = True, smooth_k: bool = True,
+                       bf16_p: bool = False) -> np.ndarray:
     """Quantised attention.  q, k, v: float32 [B, N, H, d] holding bf16 values.
 
     ``quant``: the dict of :func:`oracle.quantize` if already computed.  ``rows``:
     query tokens to evaluate (rows are independent given the quantised K and V).
     The switches ``int8_qk``, ``fp8_p`` and ``fp8_v`` replace a quantised operand by
     its exact value; with all three off the pipeline is exact online softmax.
+    ``bf16_p`` (with ``fp8_p`` off) rounds P to bf16 instead: together with
+    ``fp8_v=False`` this is the quality mode (INT8 QK^T, bf16 P.V).
     Returns fp64 [B, R, H, d]."""
+    if fp8_p and bf16_p:
+        raise ValueError("P is rounded either to e4m3 or to bf16, not both")
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     v = np.asarray(v, dtype=F32)
@@ -169,7 +184,12 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                     with np.errstate(invalid="ignore"):
                         alpha = _exp2_f32((m - m_new).astype(F32)).astype(np.float64)
                     alpha = np.where(np.isneginf(m), 0.0, alpha)
-                    pq = e4m3_decode(e4m3_encode(p)) if fp8_p else p.astype(np.float64)
+                    if fp8_p:
+                        pq = e4m3_decode(e4m3_encode(p))
+                    elif bf16_p:
+                        pq = bf16_round(p).astype(np.float64)
+                    else:
+                        pq = p.astype(np.float64)
                     l = alpha * l + p.astype(np.float64).sum(axis=1)
                     acc = alpha[:, None] * acc + pq @ vv[t0:t1]
                     m = m_new

@@ -158,3 +158,46 @@ def test_error_budget_sanity_on_tiny_workload():
     assert int8_only < int8_raw                      # smoothing helps
     # FP8 rounding of P and V (relative step 2^-3) dominates the full pipeline
     assert 0.02 < full < 0.06
+
+
+# ---- quality mode: INT8 Q.K^T, P rounded to bf16, V unquantised ----
+
+def _quality(q, k, v, **kw):
+    return attention_pipeline(q, k, v, fp8_p=False, bf16_p=True, fp8_v=False, **kw)
+
+
+def test_quality_uniform_case_is_exact_token_mean():
+    # identical key rows: every p is 448, which bf16 holds exactly, so the output is
+    # the fp64 token mean of the bf16 V values
+    q, k, v = _qkv(1, 150, 2, 32, seed=21)
+    k[:] = k[:, :1]
+    o = _quality(q, k, v, kv_tile=64)
+    want = v.astype(np.float64).mean(axis=1)                   # [B, H, d]
+    assert np.abs(o - want[:, None]).max() < 1e-12 * max(1.0, np.abs(want).max())
+
+
+def test_quality_p_rounding_is_bf16_and_bounded():
+    # against the same pipeline with unrounded p: the only difference is the bf16
+    # rounding of p (relative step 2^-8, error at most 2^-9 of each p), so each output
+    # moves by at most 2^-9 * max|v| of its head, and it does move
+    q, k, v = _qkv(1, 257, 2, 64, seed=22, kbias=2.0)
+    oq = _quality(q, k, v, kv_tile=128)
+    oe = attention_pipeline(q, k, v, kv_tile=128, fp8_p=False, fp8_v=False)
+    vmax = np.abs(v.astype(np.float64)).max(axis=(1, 3))        # [B, H]
+    diff = np.abs(oq - oe)
+    assert (diff <= 2.0 ** -9 * vmax[:, None, :, None] * (1 + 1e-9)).all()
+    assert diff.max() > 0
+    # e4m3 rounding of p instead would exceed that bound somewhere
+    o8 = attention_pipeline(q, k, v, kv_tile=128, fp8_v=False)
+    assert (np.abs(o8 - oe) > 2.0 ** -9 * vmax[:, None, :, None]).any()
+
+
+def test_quality_mode_error_budget():
+    # with P.V in 16 bits the error left is the INT8 Q.K^T quantisation: well below the
+    # speed mode's and within 0.02 of exact attention on the tiny workload
+    w = workloads.get("tiny")
+    q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+    ex = attention_exact(q, k, v)
+    rq = oracle.rel_l2(_quality(q, k, v, kv_tile=128), ex)
+    rs = oracle.rel_l2(attention_pipeline(q, k, v, kv_tile=128), ex)
+    assert rq < 0.02 and rq < 0.6 * rs
