@@ -49,6 +49,32 @@ def quant_bytes(w) -> float:
     return 9.0 * E
 
 
+def measure_quality(w, steps, warmup):
+    """Whole-step time of the quality mode (INT8 Q.K^T, bf16 P.V) on workload w."""
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
+    out = torch.empty_like(q)
+    ws = torch.empty(sage.sage_workspace_bytes_ex(w.B, w.H, w.N, w.d, "bf16"), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16")
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16")
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return {"N": w.N, "ms_per_step": round(ms, 4), "tops": round(w.ops / (ms * 1e-3) / 1e12, 2)}
+
+
 def measure(w, steps, warmup):
     import torch
     import workloads
@@ -256,6 +282,13 @@ def main():
                            "mfma_util": round(rs["attn_tops"] / PEAK_TOPS, 4),
                            "quant_ms": round(rs["quant_ms"], 4),
                            "quant_gbs": round(rs["quant_gbs"], 1)}
+    quality = {}
+    if not args.no_sweep:
+        for name in [w.name] + SWEEP:
+            wq = workloads.get(name)
+            print(f"[bench] quality mode {name} N={wq.N}", file=sys.stderr, flush=True)
+            quality[name] = measure_quality(wq, args.steps if name == w.name else max(3, args.steps // 4),
+                                            args.warmup if name == w.name else 2)
     info = sage.sage_kernel_info()
     traffic = recorded_traffic(w.name)
     line = {
@@ -283,6 +316,7 @@ def main():
                      "kernel": "k_attn<%d>" % w.d,
                      "algorithmic_bytes": 5 * w.B * w.H * w.N * w.d},
         "sweep": sweep,
+        "quality_mode": quality,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

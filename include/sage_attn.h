@@ -66,6 +66,12 @@ enum {
     SAGE_EHIP = -5             /* a kernel launch failed (HIP error text in sage_last_error) */
 };
 
+/* Precision of the P.V product (sage_attn_fwd_ex, sage_workspace_bytes_ex). */
+enum {
+    SAGE_PV_FP8 = 0,           /* speed: P and V in FP8 e4m3 (the default path) */
+    SAGE_PV_BF16 = 1           /* quality: P rounded to bf16, V unquantised bf16 */
+};
+
 typedef struct sage_info {
     int block_m;               /* query rows per attention workgroup */
     int kv_tile;               /* keys per online-softmax step (the tile T) */
@@ -90,6 +96,8 @@ int64_t sage_padded_tokens(int N);
  * operands plus that scratch).  Status as for the calls they size. */
 int sage_quant_scratch_bytes(int B, int H, int N, int d, size_t* bytes);
 int sage_workspace_bytes(int B, int H, int N, int d, size_t* bytes);
+/* Workspace bytes of sage_attn_fwd_ex for pv_mode (SAGE_EINVAL for another mode). */
+int sage_workspace_bytes_ex(int B, int H, int N, int d, int pv_mode, size_t* bytes);
 
 /*
  * sage_quant_qk - the quantisation pass.
@@ -141,6 +149,27 @@ int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
                   int B, int H, int N, int d, float sm_scale,
                   const sage_strides strides[4], void* stream,
                   void* workspace, size_t workspace_bytes);
+
+/*
+ * sage_attn_fwd_ex - sage_attn_fwd with a choice of P.V precision.  The pages note
+ * that quantised attention schemes offer a quality-first setting beside the
+ * speed-first one (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速",
+ * section 4.3) and advise 16-bit attention for critical work (apatero page
+ * "TeaCache和SageAttention优化实现更快的AI图像生成", section on when quality differences
+ * appear).
+ *   SAGE_PV_FP8:  identical to sage_attn_fwd.
+ *   SAGE_PV_BF16: Q.K^T, k_mean, the scales and the softmax arithmetic are those of
+ *     sage_attn_fwd (same p = 448 * 2^(s - m)); p is rounded to bf16 (nearest even)
+ *     instead of e4m3, V is not quantised (its bf16 values, transposed to
+ *     channel-major in the workspace), acc += P16 . V16 on bf16 matrix cores with fp32
+ *     accumulation, O = acc / l.  The workspace (sage_workspace_bytes_ex) then holds
+ *     bf16 V [B][H][d][Npad] in place of v_f8; v_scale is not written.
+ * Any other pv_mode returns SAGE_EINVAL.
+ */
+int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                     int B, int H, int N, int d, float sm_scale,
+                     const sage_strides strides[4], int pv_mode, void* stream,
+                     void* workspace, size_t workspace_bytes);
 
 /*
  * sage_debug_qk_i32 - diagnostic: the exact int32 S = Q8.K8^T tiles of head (b, h),

@@ -9,9 +9,10 @@ import os
 import torch
 
 __all__ = ["SageError", "lib_path", "load", "sage_last_error", "sage_kernel_info",
-           "sage_padded_tokens", "sage_workspace_bytes", "sage_quant_scratch_bytes",
-           "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd", "sage_debug_qk_i32",
-           "sage_debug_e4m3", "EXPORTS", "STATUS"]
+           "sage_padded_tokens", "sage_workspace_bytes", "sage_workspace_bytes_ex",
+           "sage_quant_scratch_bytes", "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd",
+           "sage_attn_fwd_ex", "sage_debug_qk_i32", "sage_debug_e4m3", "EXPORTS", "STATUS",
+           "SAGE_PV_FP8", "SAGE_PV_BF16", "PV_MODES"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(HERE, "libsage_attn.so")
@@ -20,8 +21,12 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_EINVAL", -2: "SAGE_EUNSUPPORTED", -3: "SAGE_EA
           -4: "SAGE_EWORKSPACE", -5: "SAGE_EHIP"}
 
 EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
-           "sage_quant_scratch_bytes", "sage_workspace_bytes", "sage_quant_qk",
-           "sage_attn_fwd_prequant", "sage_attn_fwd", "sage_debug_qk_i32", "sage_debug_e4m3"]
+           "sage_quant_scratch_bytes", "sage_workspace_bytes", "sage_workspace_bytes_ex",
+           "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd", "sage_attn_fwd_ex",
+           "sage_debug_qk_i32", "sage_debug_e4m3"]
+
+SAGE_PV_FP8, SAGE_PV_BF16 = 0, 1
+PV_MODES = {"fp8": SAGE_PV_FP8, "bf16": SAGE_PV_BF16}
 
 
 class SageError(RuntimeError):
@@ -50,6 +55,7 @@ _SIGS = {
     "sage_padded_tokens": (ctypes.c_int64, [_I]),
     "sage_quant_scratch_bytes": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "sage_workspace_bytes": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "sage_workspace_bytes_ex": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "sage_quant_qk": (_I, [_P, _P, _P, ctypes.POINTER(sage_strides), ctypes.POINTER(sage_strides),
                            ctypes.POINTER(sage_strides), _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -57,6 +63,8 @@ _SIGS = {
                                     _I, _I, _I, _I, ctypes.c_float, _P]),
     "sage_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
                            ctypes.POINTER(sage_strides), _P, _P, _SZ]),
+    "sage_attn_fwd_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
+                              ctypes.POINTER(sage_strides), _I, _P, _P, _SZ]),
     "sage_debug_qk_i32": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "sage_debug_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
 }
@@ -106,6 +114,21 @@ def sage_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     n = _SZ()
     _check(load().sage_workspace_bytes(B, H, N, d, ctypes.byref(n)))
     return n.value
+
+
+def sage_workspace_bytes_ex(B: int, H: int, N: int, d: int, pv: str = "fp8") -> int:
+    n = _SZ()
+    _check(load().sage_workspace_bytes_ex(B, H, N, d, _pv(pv), ctypes.byref(n)))
+    return n.value
+
+
+def _pv(pv) -> int:
+    """'fp8' / 'bf16' (or the SAGE_PV_* value) -> the C enum value."""
+    if isinstance(pv, str):
+        if pv not in PV_MODES:
+            raise ValueError(f"pv must be one of {sorted(PV_MODES)}, got {pv!r}")
+        return PV_MODES[pv]
+    return int(pv)
 
 
 def sage_quant_scratch_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -211,6 +234,16 @@ def sage_attn_fwd(q, k, v, out: torch.Tensor | None = None, sm_scale: float | No
     """O = softmax(Q K^T * sm_scale) V by the quantised path.  q, k, v, out: bf16 CUDA
     views in ``layout`` ('bnhd' = [B, N, H, d], 'bhnd' = [B, H, N, d]); any strides with
     a contiguous channel dimension (e.g. slices of a fused qkv tensor)."""
+    return sage_attn_fwd_ex(q, k, v, out=out, sm_scale=sm_scale, layout=layout,
+                            workspace=workspace, pv="fp8", _entry="sage_attn_fwd")
+
+
+def sage_attn_fwd_ex(q, k, v, out: torch.Tensor | None = None, sm_scale: float | None = None,
+                     layout: str = "bnhd", workspace: torch.Tensor | None = None,
+                     pv="fp8", _entry: str = "sage_attn_fwd_ex") -> torch.Tensor:
+    """sage_attn_fwd with the P.V precision ``pv``: 'fp8' (speed, the default path) or
+    'bf16' (quality: P rounded to bf16, V unquantised)."""
+    mode = _pv(pv)
     for n, t in (("q", q), ("k", k), ("v", v)):
         _bf16_cuda(n, t)
     (B, H, N, d), sq = _dims(q, layout)
@@ -226,12 +259,17 @@ def sage_attn_fwd(q, k, v, out: torch.Tensor | None = None, sm_scale: float | No
     if do != (B, H, N, d):
         raise ValueError("out must have the shape of q")
     if workspace is None:
-        workspace = torch.empty(sage_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(sage_workspace_bytes_ex(B, H, N, d, mode), dtype=torch.uint8, device=dev)
     sm = _default_scale(d) if sm_scale is None else float(sm_scale)
     strides = (sage_strides * 4)(sq, sk, sv, so)
-    _check(load().sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                B, H, N, d, sm, strides, _stream(dev), workspace.data_ptr(),
-                                workspace.numel()))
+    if _entry == "sage_attn_fwd":
+        _check(load().sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    B, H, N, d, sm, strides, _stream(dev), workspace.data_ptr(),
+                                    workspace.numel()))
+    else:
+        _check(load().sage_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, H, N, d, sm, strides, mode, _stream(dev),
+                                       workspace.data_ptr(), workspace.numel()))
     return out
 
 

@@ -3,20 +3,19 @@
 // FP8 e4m3, P.V on FP8 matrix cores, bf16 output (juejin page "MiniMax H3 接入
 // SageAttention 实测加速", section 一: INT8 for QK, FP8 for PV; bjdmk page
 // "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2: blockwise computation
-// that never writes the score matrix out).
+// that never writes the score matrix out).  A quality mode keeps P.V in bf16 (P rounded
+// to bf16, V unquantised) on bf16 matrix cores (the quality-first setting of the same
+// bjdmk page, section 4.3).
 //
 // Work decomposition
-//   workgroup = 4 waves = 128 query rows of one (b, h), one workgroup per CU and one
-//   wave per SIMD (up to 512 registers per lane).  Each wave owns 2 groups of 16
-//   queries.  Keys are visited in tiles of 128; K tiles (128 x d int8) and V tiles
-//   (d x 128 e4m3, channel-major) are copied into two LDS rings of 4 buffers each,
-//   3 tiles ahead of use, and shared by the 4 waves.
-//
-// Software pipeline (one step per key tile t): while the VALU runs the online softmax
-// of tile t for both query groups, the matrix cores compute S of tile t+1 and P.V of
-// tile t-1; the instruction stream of the step is written out explicitly (34 VALU
-// chunks with the 48 matrix-core instructions and their LDS operand loads between
-// them), so one wave keeps both units busy.
+//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 2 groups of 16
+//   queries; 2 workgroups per CU (2 waves per SIMD).  Keys are visited in tiles of 128.
+//   K tiles (128 x d int8) and V tiles (d x 128, channel-major) are copied HBM -> LDS
+//   by LDS DMA (global_load_lds_dwordx4, no registers involved) and shared by the 4
+//   waves: speed mode double-buffers (K, V) stages, one tile ahead of use; quality mode
+//   double-buffers K and refills a single bf16 V buffer while S and the softmax of the
+//   same tile are computed.  Waits are counted (s_waitcnt vmcnt(n) + s_barrier), so a
+//   wave only waits for the copies it needs.
 //
 // Register layouts (16x16 matrix-core tiles; lane l, r = l % 16, g = l / 16)
 //   S^T = K . Q^T with v_mfma_i32_16x16x64_i8: the row operand is 16 keys, the column
@@ -24,11 +23,13 @@
 //   Row j of key sub-tile kt is mapped to tile key 32*(j/4) + 4*kt + j%4, so lane l ends
 //   up holding, for its query r, the 32 consecutive tile keys 32g .. 32g+31 (register i
 //   of sub-tile kt = key 32g + 4kt + i).  Those 32 keys lie in one 64-key scale block.
-//   O^T = V^T . P^T with v_mfma_f32_16x16x128_f8f6f4: the column operand of lane l is
-//   32 bytes of P for query r over keys 32g .. 32g+31, exactly the values the lane
-//   already holds, so P never leaves its registers; the row operand is 32 bytes of
-//   channel-major V (channel 16*dt + r, the same 32 keys).  Output: lane l holds
-//   O[query r][channel 16*dt + 4g + i].
+//   O^T = V^T . P^T with v_mfma_f32_16x16x128_f8f6f4 (speed): the column operand of
+//   lane l is 32 bytes of P for query r over keys 32g .. 32g+31, exactly the values the
+//   lane already holds, so P never leaves its registers; the row operand is 32 bytes of
+//   channel-major V (channel 16*dt + r, the same 32 keys).  Quality mode uses
+//   v_mfma_f32_16x16x32_bf16 four times per channel tile: step s takes the lane's keys
+//   32g + 8s .. +7 from both operands (any key order common to both operands sums the
+//   same products).  Output: lane l holds O[query r][channel 16*dt + 4g + i].
 //   Every per-query quantity (running max m, partial row sum, accumulators) is thus
 //   lane-local; only the tile maximum and the final row sum combine the 4 lanes
 //   r, r+16, r+32, r+48.
@@ -59,11 +60,21 @@ __device__ __forceinline__ int kswz(int key) {
     return (key >> 5) & 3;
 }
 __device__ __forceinline__ int vswz(int ch) { return ((ch ^ (ch >> 3)) & 1) | (ch & 6); }
+// bf16 V tile [D channels][128 keys], 256 bytes per channel: physical chunk = chunk ^
+// v16swz(channel).  A read touches channels 16*dt + r and chunks 4g + s; the map is
+// linear in channel bits 0-3 and was chosen by timing all 2^16 such maps on this
+// pattern (about 30% run at the conflict-free rate, the plain XOR with the channel at
+// half of it).
+__device__ __forceinline__ int v16swz(int ch) {
+  const int b0 = ch & 1, b1 = (ch >> 1) & 1, b2 = (ch >> 2) & 1, b3 = (ch >> 3) & 1;
+  return b1 | ((b1 ^ b2 ^ b3) << 1) | ((b1 ^ b3) << 2) | ((b0 ^ b1 ^ b2 ^ b3) << 3);
+}
 
 template <int D>
 struct Lds {
-  static constexpr int KBYTES = kKvTile * D;   // one K tile
-  static constexpr int VBYTES = D * kKvTile;   // one V tile
+  static constexpr int KBYTES = kKvTile * D;       // one K tile
+  static constexpr int VBYTES = D * kKvTile;       // one e4m3 V tile
+  static constexpr int V16BYTES = D * kKvTile * 2; // one bf16 V tile
 };
 
 // Per-lane LDS byte offsets of the matrix-core operand reads.  The swizzles depend only
@@ -121,6 +132,37 @@ struct DmaOffsets {
   }
 };
 
+// Quality mode: per-lane LDS offsets of the bf16 V reads (step s of channel tile dt is
+// voff[s] + dt * 16 * 256) and source offsets of the bf16 V tile copies.
+template <int D>
+struct LaneOffsets16 {
+  int voff[4];
+  __device__ __forceinline__ explicit LaneOffsets16(int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) voff[s] = r * 256 + 16 * ((4 * g + s) ^ v16swz(r));
+  }
+};
+
+template <int D>
+struct DmaOffsets16 {
+  static constexpr int VPW = Lds<D>::V16BYTES / 1024 / kWaves;
+  uint32_t voff[VPW];
+  __device__ __forceinline__ DmaOffsets16(int wave, int lane, int64_t npad) {
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) {
+      const int pos = (wave * VPW + j) * 1024 + lane * 16;
+      const int ch = pos / 256, pc = (pos % 256) / 16;
+      voff[j] = (uint32_t)(ch * npad * 2 + (pc ^ v16swz(ch & 15)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue_v(const uint8_t* __restrict__ vtile, uint8_t* vlds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < VPW; ++j)
+      __builtin_amdgcn_global_load_lds(vtile + voff[j], (lds_ptr_t)(vlds + (wave * VPW + j) * 1024), 16, 0, 0);
+  }
+};
+
 // Column operands (queries) of S^T for this wave: lane l holds query row `qrow0 + 16*gq
 // + r`, bytes 64*kk + 16*g .. +15.
 template <int D>
@@ -164,30 +206,78 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const v4i (&qfr)[G]
   }
 }
 
+// The P operand of one query group: e4m3 (word kt = keys 32g + 4kt .. +3), or bf16
+// (words 2kt and 2kt+1 = keys 32g + 4kt .. +3, in w[kt / 4]).
+template <int PV> struct PTile;
+template <> struct PTile<kPvFp8> { v8i w; };
+template <> struct PTile<kPvBf16> { v8i w[2]; };
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 (round to nearest even), first value in the low half.
+__device__ __forceinline__ int pk_bf16(float a, float b) {
+  return __builtin_bit_cast(int, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
+// Rounds the p of keys 32g + 4kt .. +3 into P.  The e4m3 conversions overwrite both
+// halves of the word, so its previous contents only serve as the operand they replace.
+template <int PV>
+__device__ __forceinline__ void store_p(PTile<PV>& P, int kt, const float (&p)[4]) {
+  if constexpr (PV == kPvFp8) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P.w[kt], false);
+    P.w[kt] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+  } else {
+    P.w[kt >> 2][2 * (kt & 3)] = pk_bf16(p[0], p[1]);
+    P.w[kt >> 2][2 * (kt & 3) + 1] = pk_bf16(p[2], p[3]);
+  }
+}
+
 // acc[gq][dt] += V^T(channels 16dt..16dt+15) . P[gq]^T for both groups.
 template <int D>
-__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, const v8i (&P)[G], const LaneOffsets<D>& lo,
-                                        v4f (&acc)[G][D / 16]) {
+__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, const PTile<kPvFp8> (&P)[G],
+                                        const LaneOffsets<D>& lo, v4f (&acc)[G][D / 16]) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     const v8i vf = load_vfrag<D>(vbuf, dt, lo);
 #pragma unroll
     for (int gq = 0; gq < G; ++gq)
-      acc[gq][dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, P[gq], acc[gq][dt], 0, 0, 0, 0, 0, 0);
+      acc[gq][dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, P[gq].w, acc[gq][dt], 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// Quality mode: the same product with bf16 P and bf16 V, four 32-key steps per channel
+// tile; step s uses the lane's keys 32g + 8s .. +7 of both operands.
+template <int D>
+__device__ __forceinline__ void pv_tile16(const uint8_t* vbuf, const PTile<kPvBf16> (&P)[G],
+                                          const LaneOffsets16<D>& lo, v4f (&acc)[G][D / 16]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const v8bf vf = __builtin_bit_cast(v8bf, *(const v4i*)(vbuf + lo.voff[s] + dt * 16 * 256));
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) {
+        const v4i pw = (s & 1) ? __builtin_shufflevector(P[gq].w[s >> 1], P[gq].w[s >> 1], 4, 5, 6, 7)
+                               : __builtin_shufflevector(P[gq].w[s >> 1], P[gq].w[s >> 1], 0, 1, 2, 3);
+        acc[gq][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(v8bf, pw), acc[gq][dt], 0, 0, 0);
+      }
+    }
   }
 }
 
 // Online-softmax update of one 16-query group for one tile, not interleaved (used at the
 // ends of the pipeline and for the ragged last tile).  S is consumed (converted to fp32
 // exactly: |S| < 2^24); c = fp32(q factor * k_scale) of this lane's keys.  Produces the
-// e4m3 P operand, updates the running max m and this lane's partial row sum, and
+// P operand, updates the running max m and this lane's partial row sum, and
 // returns alpha = 2^(m_old - m_new), the factor the accumulators need.  When MASKED,
 // keys at tile index >= nvalid are removed by giving them the logit -inf; a lane whose
 // c is 0 then uses x = 0 and c = 1 for its valid keys, which yields the same s = 0 and
 // p = 448 * 2^-m without forming -inf * 0.
-template <bool MASKED>
+template <bool MASKED, int PV>
 __device__ __forceinline__ float softmax_group(v4i (&S)[8], float c, int nvalid, float log2_pscale,
-                                               float& m, float& lpart, v8i& P, int g) {
+                                               float& m, float& lpart, PTile<PV>& P, int g) {
   float xf[8][4];
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt)
@@ -223,20 +313,11 @@ __device__ __forceinline__ float softmax_group(v4i (&S)[8], float c, int nvalid,
       p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kt][i], c, nb));
       lsum += p[i];
     }
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-    P[kt] = w;
+    store_p<PV>(P, kt, p);
   }
   lpart = alpha * lpart + lsum;
   m = m_new;
   return alpha;
-}
-
-// Marks P (and the row-sum state) as used at this point, so that the compiler keeps the
-// softmax work that produces it inside the pipeline step it was interleaved with.
-__device__ __forceinline__ void materialize(const v8i& P, float l) {
-  asm volatile("" : : "v"(P[0]), "v"(P[1]), "v"(P[2]), "v"(P[3]), "v"(P[4]), "v"(P[5]),
-               "v"(P[6]), "v"(P[7]), "v"(l));
 }
 
 // acc *= alpha, skipped when no lane's maximum moved (multiplying by exactly 1).
@@ -250,10 +331,11 @@ __device__ __forceinline__ void rescale(v4f (&acc)[D / 16], float alpha) {
 
 // Online-softmax update of both query groups for one full tile (no masking): integer
 // row max (exact, no NaN handling), fp32 conversion (exact: |S| < 2^24), exp2 of the
-// fused multiply-add, e4m3 packing into P, independent partial row sums.  Same
+// fused multiply-add, rounding into P, independent partial row sums.  Same
 // arithmetic as softmax_group<false>; the two groups' work is interleaved for ILP.
+template <int PV>
 __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G], float log2_pscale,
-                                             float (&m)[G], float (&lpart)[G], v8i (&P)[G],
+                                             float (&m)[G], float (&lpart)[G], PTile<PV> (&P)[G],
                                              float (&alpha)[G]) {
   int xmi[G];
 #pragma unroll
@@ -286,10 +368,7 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
       for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[gq][kt][i], c[gq], nb[gq]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
-      // the previous contents of P[gq][kt] are overwritten by the two conversions
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[gq][kt], false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-      P[gq][kt] = w;
+      store_p<PV>(P[gq], kt, p);
     }
   }
 #pragma unroll
@@ -336,9 +415,15 @@ struct Ring {
   __device__ __forceinline__ uint8_t* vbuf(int t) const { return smem + (t % kStages) * STAGE + Lds<D>::KBYTES; }
 };
 
-template <int D>
+template <int D, int PV>
+struct AttnSmem {
+  static constexpr int BYTES = PV == kPvFp8 ? kStages * Ring<D>::STAGE
+                                            : 2 * Lds<D>::KBYTES + Lds<D>::V16BYTES;
+};
+
+template <int D, int PV>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * Ring<D>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[AttnSmem<D, PV>::BYTES];
 
   // workgroup-uniform indices kept in scalar registers (readfirstlane), so that the
   // per-tile k_scale reads are scalar loads and never wait on the vector-memory counter
@@ -353,38 +438,18 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
   const int qrow0 = qb * kBlockM + wave * (G * 16);
   const int64_t nblk = a.npad / kQuantBlock;
 
-  const Ring<D> ring{smem};
   const LaneOffsets<D> lo(lane);
   const DmaOffsets<D> dma(wave, lane, a.npad);
   const int8_t* kh = a.k_i8 + bh * a.npad * D;
-  const uint8_t* vh = a.v_f8 + bh * D * a.npad;
   typedef const __attribute__((address_space(4))) float* const_f32_ptr;
   // k_scale through the constant address space: scalar loads (counted by lgkmcnt)
   const const_f32_ptr ksh = (const_f32_ptr)(a.k_scale + bh * nblk);
   const int ntiles = (a.N + kKvTile - 1) / kKvTile;
   const int tail = a.N - (ntiles - 1) * kKvTile;     // keys in the last tile (1..128)
   const int nfull = (tail == kKvTile) ? ntiles : ntiles - 1;   // tiles without masking
-  auto copy_tile = [&](int t) {
-    if (t < ntiles) {
-      dma.issue_k(kh + (int64_t)t * kKvTile * D, ring.kbuf(t), wave);
-      dma.issue_v(vh + (int64_t)t * kKvTile, ring.vbuf(t), wave);
-    }
-  };
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) copy_tile(t);
 
-  v4i qfr[G][D / 64];
-  load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
   float qf[G], m[G], lpart[G], alpha[G], c[G];
   v4f acc[G][D / 16];
-#pragma unroll
-  for (int gq = 0; gq < G; ++gq) {
-    qf[gq] = a.q_scale[bh * nblk + (qrow0 + 16 * gq) / kQuantBlock] * a.log2e_scale;
-    m[gq] = -INFINITY;
-    lpart[gq] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[gq][dt] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef const __attribute__((address_space(4))) f32x2* const_f32x2_ptr;
   auto scale_products = [&](int t) {
@@ -394,32 +459,93 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) c[gq] = qf[gq] * ks;
   };
-
-  v4i S[G][8];
-  v8i P[G];
-  constexpr int KEEP = (kStages - 2) * DmaOffsets<D>::PER_TILE;
-  for (int t = 0; t < nfull; ++t) {
-    // tile t has landed once only the copies of the kStages-2 later tiles may be in flight
-    if (t + kStages - 2 < ntiles) tile_barrier<KEEP>();
-    else tile_barrier<0>();
-    copy_tile(t + kStages - 1);        // into the stage all waves finished in step t-1
-    scale_products(t);
-    qk_tile<D>(ring.kbuf(t), qfr, lo, S);
-    softmax_tile(S, c, a.log2_pscale, m, lpart, P, alpha);
-#pragma unroll
-    for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
-    pv_tile<D>(ring.vbuf(t), P, lo, acc);
-  }
-  if (nfull < ntiles) {                // last tile: keys >= N masked
-    tile_barrier<0>();
-    scale_products(nfull);
-    qk_tile<D>(ring.kbuf(nfull), qfr, lo, S);
+  auto init_state = [&]() {
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
-      alpha[gq] = softmax_group<true>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
-      rescale<D>(acc[gq], alpha[gq]);
+      qf[gq] = a.q_scale[bh * nblk + (qrow0 + 16 * gq) / kQuantBlock] * a.log2e_scale;
+      m[gq] = -INFINITY;
+      lpart[gq] = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[gq][dt] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    pv_tile<D>(ring.vbuf(nfull), P, lo, acc);
+  };
+  v4i qfr[G][D / 64];
+  v4i S[G][8];
+  PTile<PV> P[G];
+
+  if constexpr (PV == kPvFp8) {
+    const Ring<D> ring{smem};
+    const uint8_t* vh = a.v_f8 + bh * D * a.npad;
+    auto copy_tile = [&](int t) {
+      if (t < ntiles) {
+        dma.issue_k(kh + (int64_t)t * kKvTile * D, ring.kbuf(t), wave);
+        dma.issue_v(vh + (int64_t)t * kKvTile, ring.vbuf(t), wave);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t) copy_tile(t);
+    load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
+    init_state();
+    constexpr int KEEP = (kStages - 2) * DmaOffsets<D>::PER_TILE;
+    for (int t = 0; t < nfull; ++t) {
+      // tile t has landed once only the copies of the kStages-2 later tiles may be in flight
+      if (t + kStages - 2 < ntiles) tile_barrier<KEEP>();
+      else tile_barrier<0>();
+      copy_tile(t + kStages - 1);        // into the stage all waves finished in step t-1
+      scale_products(t);
+      qk_tile<D>(ring.kbuf(t), qfr, lo, S);
+      softmax_tile<PV>(S, c, a.log2_pscale, m, lpart, P, alpha);
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
+      pv_tile<D>(ring.vbuf(t), P, lo, acc);
+    }
+    if (nfull < ntiles) {                // last tile: keys >= N masked
+      tile_barrier<0>();
+      scale_products(nfull);
+      qk_tile<D>(ring.kbuf(nfull), qfr, lo, S);
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) {
+        alpha[gq] = softmax_group<true, PV>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
+        rescale<D>(acc[gq], alpha[gq]);
+      }
+      pv_tile<D>(ring.vbuf(nfull), P, lo, acc);
+    }
+  } else {
+    // K double-buffered, one bf16 V buffer.  Step t: barrier (K(t) landed, every wave
+    // done with step t-1), copy V(t) and K(t+1), S and softmax of tile t, barrier (V(t)
+    // landed; K(t+1) may still be in flight), P.V of tile t.
+    uint8_t* vbuf = smem + 2 * Lds<D>::KBYTES;
+    auto kbuf = [&](int t) { return smem + (t & 1) * Lds<D>::KBYTES; };
+    const LaneOffsets16<D> lo16(lane);
+    const DmaOffsets16<D> dma16(wave, lane, a.npad);
+    const uint8_t* vh = (const uint8_t*)(a.v16 + bh * D * a.npad);
+    auto copy_k = [&](int t) {
+      if (t < ntiles) dma.issue_k(kh + (int64_t)t * kKvTile * D, kbuf(t), wave);
+    };
+    copy_k(0);
+    load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
+    init_state();
+    auto step = [&](int t, bool masked) {
+      tile_barrier<0>();
+      dma16.issue_v(vh + (int64_t)t * kKvTile * 2, vbuf, wave);
+      copy_k(t + 1);
+      scale_products(t);
+      qk_tile<D>(kbuf(t), qfr, lo, S);
+      if (!masked) {
+        softmax_tile<PV>(S, c, a.log2_pscale, m, lpart, P, alpha);
+      } else {
+#pragma unroll
+        for (int gq = 0; gq < G; ++gq)
+          alpha[gq] = softmax_group<true, PV>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
+      }
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
+      if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW>();
+      else tile_barrier<0>();
+      pv_tile16<D>(vbuf, P, lo16, acc);
+    };
+    for (int t = 0; t < nfull; ++t) step(t, false);
+    if (nfull < ntiles) step(nfull, true);
   }
 
   // epilogue: total row sum over the 4 lanes of each query, normalise, V scale, bf16
@@ -436,11 +562,12 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const int c0 = 16 * dt + 4 * g;
-        uint32_t h0 = f32_to_bf16_rne(acc[gq][dt][0] * vsh[c0 + 0] * rl);
-        uint32_t h1 = f32_to_bf16_rne(acc[gq][dt][1] * vsh[c0 + 1] * rl);
-        uint32_t h2 = f32_to_bf16_rne(acc[gq][dt][2] * vsh[c0 + 2] * rl);
-        uint32_t h3 = f32_to_bf16_rne(acc[gq][dt][3] * vsh[c0 + 3] * rl);
-        *(uint2*)(orow + c0) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = PV == kPvFp8 ? acc[gq][dt][i] * vsh[c0 + i] * rl : acc[gq][dt][i] * rl;
+        *(uint2*)(orow + c0) = make_uint2(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
+                                          f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16));
       }
     }
   }
@@ -481,10 +608,17 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int nqb = (int)(a.npad / kBlockM);
   const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.H);
-  if (a.d == 64)
-    hipLaunchKernelGGL(k_attn<64>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attn<128>, dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.pv == kPvBf16) {
+    if (a.d == 64)
+      hipLaunchKernelGGL((k_attn<64, kPvBf16>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn<128, kPvBf16>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else {
+    if (a.d == 64)
+      hipLaunchKernelGGL((k_attn<64, kPvFp8>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn<128, kPvFp8>), dim3(grid), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -503,8 +637,10 @@ hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_
 
 // explicit instantiations: the host pass does not always emit launch stubs for kernel
 // templates that are only named inside hipLaunchKernelGGL
-template __global__ void k_attn<64>(AttnArgs);
-template __global__ void k_attn<128>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16>(AttnArgs);
 template __global__ void k_debug_qk<64>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,
                                         int64_t, int, int, int, int32_t* __restrict__);
 template __global__ void k_debug_qk<128>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,

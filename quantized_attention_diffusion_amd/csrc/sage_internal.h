@@ -18,6 +18,10 @@ constexpr int kMinWavesPerSimd = 2; // occupancy the attention kernel is compile
 constexpr float kPScale = 448.0f;   // static scale of P before e4m3 rounding
 constexpr int kMaxStatsChunks = 128; // partial-statistics rows per (b, h) in the quantisation pass
 
+// Precision of the P.V product: P in e4m3 with per-channel e4m3 V (speed), or P in
+// bf16 with the unquantised bf16 V (quality).
+enum PvMode { kPvFp8 = 0, kPvBf16 = 1 };
+
 struct Strides { int64_t b, h, n; };
 
 inline int64_t padded_tokens(int n) {
@@ -46,8 +50,10 @@ struct QuantArgs {
   int8_t* k_i8;
   float* k_scale;
   uint16_t* k_mean;
-  uint8_t* v_f8;
+  uint8_t* v_f8;       // kPvFp8: e4m3 codes [B][H][d][Npad]
   float* v_scale;
+  uint16_t* v16;       // kPvBf16: bf16 V [B][H][d][Npad]
+  int pv;              // PvMode
   double* ksum_part;   // [B*H][chunks][d]
   float* vmax_part;    // [B*H][chunks][d]
   float* v_inv;        // [B*H][d]
@@ -61,6 +67,8 @@ struct AttnArgs {
   const float* k_scale;
   const uint8_t* v_f8;
   const float* v_scale;
+  const uint16_t* v16;
+  int pv;              // PvMode
   uint16_t* out;
   Strides so;
   int B, H, N, d;

@@ -60,7 +60,9 @@ __device__ __forceinline__ void load_block(const uint16_t* base, int64_t stride_
   }
 }
 
-template <int D>
+// NEED_V: the speed mode also needs the per-channel max |V| (e4m3 V scales); the
+// quality mode keeps V in bf16 and skips it.
+template <int D, bool NEED_V>
 __global__ __launch_bounds__(256) void k_quant_q_stats(
     const uint16_t* __restrict__ q, Strides sq, const uint16_t* __restrict__ k, Strides sk,
     const uint16_t* __restrict__ v, Strides sv, int H, int N, int64_t npad, int blocks_per_chunk,
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
     uint4 qw[RPT], kw[RPT], vw[RPT];
     load_block<RPT, RPI>(qb, sq.n, row0, r, N, qw);
     load_block<RPT, RPI>(kb, sk.n, row0, r, N, kw);
-    load_block<RPT, RPI>(vb, sv.n, row0, r, N, vw);
+    if constexpr (NEED_V) load_block<RPT, RPI>(vb, sv.n, row0, r, N, vw);
     float x[RPT][8];
     uint2 codes[RPT];
 #pragma unroll
@@ -103,13 +105,15 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
     if (t == 0) q_scale[bh * nblk + blk] = scale;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      float kx[8], vx[8];
+      float kx[8];
       bf16x8_to_f32(kw[i], kx);
-      bf16x8_to_f32(vw[i], vx);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        s[j] += (double)kx[j];
-        vm[j] = fmaxf(vm[j], fabsf(vx[j]));
+      for (int j = 0; j < 8; ++j) s[j] += (double)kx[j];
+      if constexpr (NEED_V) {
+        float vx[8];
+        bf16x8_to_f32(vw[i], vx);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vm[j] = fmaxf(vm[j], fabsf(vx[j]));
       }
     }
   }
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
 // One workgroup per (b, h): 1024 threads = D channels x (1024 / D) slices of the
 // partial rows, combined through LDS in slice order.
 constexpr int kFinalizeThreads = 1024;
-template <int D>
+template <int D, bool NEED_V>
 __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
     const double* __restrict__ ksum_part, const float* __restrict__ vmax_part, int chunks, int N,
     uint16_t* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
 #pragma unroll 4
   for (int i = sl; i < chunks; i += SL) {
     s += ksum_part[(bh * chunks + i) * D + c];
-    vm = fmaxf(vm, vmax_part[(bh * chunks + i) * D + c]);
+    if constexpr (NEED_V) vm = fmaxf(vm, vmax_part[(bh * chunks + i) * D + c]);
   }
   ps[sl][c] = s;
   pv[sl][c] = vm;
@@ -154,8 +158,10 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
     for (int i = 1; i < SL; ++i) { s += ps[i][c]; vm = fmaxf(vm, pv[i][c]); }
     const float mean = (float)(s / (double)N);        // fp64 divide, one rounding to fp32
     k_mean[bh * D + c] = (uint16_t)f32_to_bf16_rne(mean);
-    v_scale[bh * D + c] = vm / kPScale;               // IEEE division (0 when vm = 0)
-    v_inv[bh * D + c] = vm > 0.0f ? kPScale / vm : 0.0f;
+    if constexpr (NEED_V) {
+      v_scale[bh * D + c] = vm / kPScale;             // IEEE division (0 when vm = 0)
+      v_inv[bh * D + c] = vm > 0.0f ? kPScale / vm : 0.0f;
+    }
   }
 }
 
@@ -164,11 +170,15 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
 // owns RPT adjacent bytes of the channel-major V block: they go to LDS as one word
 // (RPT = 4) or half word (RPT = 2), in rows of VW words whose odd pitch spreads the
 // 16 channel groups of a wave over distinct banks (at most 2 lanes per bank).
-template <int D>
+//
+// V16 (quality mode): V keeps its bf16 values and is only transposed: each thread's
+// RPT tokens of a channel (2*RPT bytes) go to LDS as RPT/2 words in rows of 33 words.
+template <int D, bool V16>
 __global__ __launch_bounds__(256) void k_quant_kv(
     const uint16_t* __restrict__ k, Strides sk, const uint16_t* __restrict__ v, Strides sv,
     int H, int N, int64_t npad, const uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_f8) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_f8,
+    uint16_t* __restrict__ v16) {
   constexpr int TPR = D / 8;
   constexpr int RPI = 256 / TPR;
   constexpr int RPT = kQuantBlock / RPI;   // consecutive tokens per thread (4 or 2)
@@ -179,16 +189,19 @@ __global__ __launch_bounds__(256) void k_quant_kv(
   const int row0 = blk * kQuantBlock;
   const int tok0 = row0 + RPT * r;           // this thread's first token
   const int64_t nblk = npad / kQuantBlock;
+  constexpr int VW16 = kQuantBlock / 2 + 1;  // LDS words per channel row, bf16 (odd pitch)
   __shared__ float red[4];
-  __shared__ uint32_t vt[D * VW];
+  __shared__ uint32_t vt[D * (V16 ? VW16 : VW)];
 
   uint4 kw[RPT], vw[RPT];
   load_block<RPT, 1>(k + (int64_t)b * sk.b + (int64_t)h * sk.h + 8 * cg, sk.n, tok0, 0, N, kw);
   load_block<RPT, 1>(v + (int64_t)b * sv.b + (int64_t)h * sv.h + 8 * cg, sv.n, tok0, 0, N, vw);
   float mu[8], inv[8];
   bf16x8_to_f32(*(const uint4*)(k_mean + bh * D + 8 * cg), mu);
+  if constexpr (!V16) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) inv[j] = v_inv[bh * D + 8 * cg + j];
+    for (int j = 0; j < 8; ++j) inv[j] = v_inv[bh * D + 8 * cg + j];
+  }
 
   // ---- K - mean -> INT8 ----
   {
@@ -206,6 +219,30 @@ __global__ __launch_bounds__(256) void k_quant_kv(
     for (int i = 0; i < RPT; ++i)
       *(uint2*)(k_i8 + (bh * npad + tok0 + i) * D + 8 * cg) = codes[i];
     if (t == 0) k_scale[bh * nblk + blk] = scale;
+  }
+  if constexpr (V16) {
+    // ---- V (bf16) transposed to [channel][token] ----
+    // word w of channel j: tokens tok0 + 2w, tok0 + 2w + 1 (RPT/2 words per channel)
+#pragma unroll
+    for (int w = 0; w < RPT / 2; ++w) {
+      const uint4 a = vw[2 * w], b = vw[2 * w + 1];
+      const uint32_t ea[4] = {a.x, a.y, a.z, a.w}, eb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t lo = (ea[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        const uint32_t hi = (eb[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        vt[(8 * cg + j) * VW16 + (RPT / 2) * r + w] = lo | (hi << 16);
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = kQuantBlock * 2 / 16;        // 16-byte chunks per channel row
+#pragma unroll
+    for (int cid = t; cid < D * CPR; cid += 256) {
+      const int c = cid / CPR, part = cid % CPR;
+      const uint32_t* src = vt + c * VW16 + 4 * part;
+      *(uint4*)(v16 + (bh * D + c) * npad + row0 + 8 * part) = make_uint4(src[0], src[1], src[2], src[3]);
+    }
+    return;
   }
   // ---- V -> e4m3, transposed to [channel][token] ----
   {
@@ -254,23 +291,24 @@ __global__ void k_debug_e4m3(const float* __restrict__ x, uint8_t* __restrict__ 
   }
 }
 
-template <int D>
+template <int D, bool V16>
 static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   const int per = stats_blocks_per_chunk(a.npad);
   const int chunks = stats_chunks(a.N);
-  hipLaunchKernelGGL(k_quant_q_stats<D>, dim3(chunks, a.H, a.B), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_quant_q_stats<D, !V16>), dim3(chunks, a.H, a.B), dim3(256), 0, s,
                      a.q, a.sq, a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, per,
                      a.q_i8, a.q_scale, a.ksum_part, a.vmax_part);
-  hipLaunchKernelGGL(k_quant_finalize<D>, dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
+  hipLaunchKernelGGL((k_quant_finalize<D, !V16>), dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
                      a.ksum_part, a.vmax_part, chunks, a.N, a.k_mean, a.v_scale, a.v_inv);
-  hipLaunchKernelGGL(k_quant_kv<D>, dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_quant_kv<D, V16>), dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
                      a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, a.k_mean, a.v_inv,
-                     a.k_i8, a.k_scale, a.v_f8);
+                     a.k_i8, a.k_scale, a.v_f8, a.v16);
   return hipGetLastError();
 }
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
-  return a.d == 64 ? launch_quant_d<64>(a, s) : launch_quant_d<128>(a, s);
+  if (a.pv == kPvBf16) return a.d == 64 ? launch_quant_d<64, true>(a, s) : launch_quant_d<128, true>(a, s);
+  return a.d == 64 ? launch_quant_d<64, false>(a, s) : launch_quant_d<128, false>(a, s);
 }
 
 hipError_t launch_debug_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t s) {

@@ -84,3 +84,25 @@ def test_full_size_parity(name):
         r_gpu, r_pipe = oracle.rel_l2(o, exact), oracle.rel_l2(pipe, exact)
         print(f"    head {h}: max|gpu-pipe| = {err:.2e}  relL2 gpu {r_gpu:.4f}  pipe {r_pipe:.4f}", flush=True)
         assert r_gpu <= r_pipe + 0.002
+
+
+@pytest.mark.parametrize("name", ["flux_like", "video"])
+def test_full_size_quality_mode(name):
+    w = workloads.get(name)
+    print(f"[full quality] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
+    q, k, v = workloads.make_qkv(w)
+    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4321)
+    N = w.N
+    for h in sorted({0, int(rng.integers(1, w.H))}):
+        qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=N_ROWS, replace=False)]))
+        pipe = oracle.attention_pipeline(qh, kh, vh, kv_tile=128, rows=rows, fp8_p=False,
+                                         bf16_p=True, fp8_v=False)
+        o = to_np(out[:, rows, h:h + 1, :])
+        err = check_attention(o, pipe, f"{name} quality head {h}")
+        exact = oracle.attention_exact(qh, kh, vh, rows=rows)
+        r_gpu, r_pipe = oracle.rel_l2(o, exact), oracle.rel_l2(pipe, exact)
+        print(f"    head {h}: max|gpu-pipe| = {err:.2e}  relL2 gpu {r_gpu:.4f}  pipe {r_pipe:.4f}", flush=True)
+        assert r_gpu <= r_pipe + 0.002

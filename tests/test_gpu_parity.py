@@ -166,3 +166,45 @@ def test_e4m3_conversion_matches_oracle_encoder():
     x = np.concatenate([x, -x]).astype(np.float32)
     got = sage.sage_debug_e4m3(torch.from_numpy(x).cuda()).cpu().numpy()
     assert np.array_equal(got, oracle.e4m3_encode(x))
+
+
+# ---- quality mode: INT8 Q.K^T, bf16 P.V ----
+
+def _quality_pipe(q, k, v, **kw):
+    return oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE, fp8_p=False,
+                                     bf16_p=True, fp8_v=False, **kw)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_quality_mode_matches_oracle_pipeline(case):
+    B, N, H, d, seed, outl = case
+    print(f"[quality] {_case_id(case)}", flush=True)
+    q, k, v = random_qkv(B, N, H, d, seed, outl)
+    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16")
+    o = to_np(out)
+    pipe = _quality_pipe(q, k, v)
+    err = check_attention(o, pipe, "quality " + _case_id(case))
+    exact = oracle.attention_exact(_np(q), _np(k), _np(v))
+    assert oracle.rel_l2(o, exact) <= oracle.rel_l2(pipe, exact) + 0.002
+    print(f"    max|gpu-pipe| = {err:.2e}  relL2(gpu, exact) = {oracle.rel_l2(o, exact):.4f}", flush=True)
+
+
+def test_quality_mode_layouts_degenerate_and_fp8_entry():
+    B, N, H, d = 1, 300, 3, 128
+    q, k, v = random_qkv(B, N, H, d, seed=31)
+    ref = to_np(sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16"))
+    qkv = torch.stack([q, k, v], dim=2).cuda()
+    of = sage.sage_attn_fwd_ex(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], pv="bf16")
+    assert np.array_equal(to_np(of), ref)
+    qh, kh, vh = (t.transpose(1, 2).contiguous().cuda() for t in (q, k, v))
+    oh = sage.sage_attn_fwd_ex(qh, kh, vh, layout="bhnd", pv="bf16")
+    assert np.array_equal(to_np(oh).transpose(0, 2, 1, 3), ref)
+    # the fp8 mode of the extended entry point is sage_attn_fwd
+    a = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="fp8")
+    b = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    assert torch.equal(a, b)
+    # identical keys: every p = 448 (exact in bf16), the output is the token mean of V
+    k2 = k.clone()
+    k2[:] = k2[:, :1]
+    o2 = sage.sage_attn_fwd_ex(q.cuda(), k2.cuda(), v.cuda(), pv="bf16")
+    check_attention(to_np(o2), _quality_pipe(q, k2, v), "quality uniform")
