@@ -35,6 +35,12 @@ Readings (the pages give none of these details):
   acc and l are kept in fp64 here; they decide no code.
 * Keys at or beyond N do not exist (no padding in the oracle).
 
+Per-token scales (``quantize(..., block=1)``): every query and key token has its own
+INT8 scale, so the key factor varies within a tile.  Reading of the arithmetic: the
+key scale is applied first, y_ij = fp32(S_ij * k_scale_j); the row maximum is over
+fp32(y_ij * qf_i), and p_ij = exp2(fp32(y_ij * qf_i + nb)) with one rounding (a fused
+multiply-add).  qf_i and nb are as above.
+
 Quality mode (``bf16_p=True, fp8_p=False, fp8_v=False``): the pages mention that
 quantised attention schemes offer a quality-first setting next to the speed-first one
 (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 4.3) and that
@@ -106,9 +112,26 @@ def qk_int32(q_codes, k_codes) -> np.ndarray:
 
 
 def _fma_f32(x, c, b):
-    """fp32(x * c + b) with one rounding: x (integer-valued, |x| < 2^24) times the fp32
-    c is exact in fp64, the fp64 sum is then rounded to fp32."""
-    return (x.astype(np.float64) * c.astype(np.float64) + b.astype(np.float64)).astype(F32)
+    """fp32(x * c + b) with one rounding (round to nearest even), for x and c fp32
+    values (or integers below 2^24) and b fp32.  The product is exact in fp64 (at most
+    48 significant bits); the fp64 sum s carries an error e that the error-free
+    two-sum recovers exactly (s + e is the exact sum).  Rounding s to fp32 is then the
+    correct rounding of s + e except when s sits exactly halfway between two fp32
+    values and e is not zero: then the exact sum lies on e's side of the halfway
+    point."""
+    a = np.asarray(x, dtype=np.float64) * np.asarray(c, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    s = a + b
+    bb = s - a
+    e = (a - (s - bb)) + (b - bb)
+    r = s.astype(F32)
+    r64 = r.astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        other = np.nextafter(r, np.where(s > r64, F32(np.inf), F32(-np.inf)).astype(F32))
+        half = (r64 + other.astype(np.float64)) / 2
+        tie = (s != r64) & (s == half) & (e != 0) & np.isfinite(s)
+        toward_other = np.sign(e) == np.sign(s - r64)
+    return np.where(tie & toward_other, other, r).astype(F32)
 
 
 def _exp2_f32(x):
@@ -118,7 +141,7 @@ def _exp2_f32(x):
 def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                        quant=None, int8_qk: bool = True, fp8_p: bool = True,
                        fp8_v: bool = True, smooth_k: bool = True,
-                       bf16_p: bool = False) -> np.ndarray:
+                       bf16_p: bool = False, block: int = QUANT_BLOCK) -> np.ndarray:
     """Quantised attention.  q, k, v: float32 [B, N, H, d] holding bf16 values.
 
     ``quant``: the dict of :func:`oracle.quantize` if already computed.  ``rows``:
@@ -126,7 +149,9 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     The switches ``int8_qk``, ``fp8_p`` and ``fp8_v`` replace a quantised operand by
     its exact value; with all three off the pipeline is exact online softmax.
     ``bf16_p`` (with ``fp8_p`` off) rounds P to bf16 instead: together with
-    ``fp8_v=False`` this is the quality mode (INT8 QK^T, bf16 P.V).
+    ``fp8_v=False`` this is the quality mode (INT8 QK^T, bf16 P.V).  ``block``: tokens
+    per Q/K scale when ``quant`` is not given (``quant`` carries its own); 1 selects
+    per-token scales and their decision arithmetic.
     Returns fp64 [B, R, H, d]."""
     if fp8_p and bf16_p:
         raise ValueError("P is rounded either to e4m3 or to bf16, not both")
@@ -136,7 +161,8 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     B, N, H, d = q.shape
     sm = default_sm_scale(d) if sm_scale is None else float(sm_scale)
     if quant is None:
-        quant = quantize(q, k, v, smooth_k=smooth_k)
+        quant = quantize(q, k, v, smooth_k=smooth_k, block=block)
+    qb = int(quant.get("block", QUANT_BLOCK))
     r = _rows(N, rows)
     L = F32(sm * LOG2E)
     out = np.empty((B, len(r), H, d), dtype=np.float64)
@@ -151,7 +177,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                 vs = np.ones(d)
             if int8_qk:
                 kq = quant["k_i8"][b, h]
-                ks = quant["k_scale"][b, h][np.arange(N) // QUANT_BLOCK]        # [N]
+                ks = quant["k_scale"][b, h][np.arange(N) // qb]                 # [N]
             else:
                 kf = k[b, :, h, :].astype(np.float64)
             for c0 in range(0, len(r), 256):
@@ -159,7 +185,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                 R = len(rr)
                 if int8_qk:
                     S = qk_int32(quant["q_i8"][b, h][rr], kq)                 # [R, N]
-                    qs = quant["q_scale"][b, h][rr // QUANT_BLOCK]
+                    qs = quant["q_scale"][b, h][rr // qb]
                     qf = (qs * L).astype(F32)                                 # [R]
                 else:
                     S = (q[b, rr, h, :].astype(np.float64) @ kf.T) * (sm * LOG2E)
@@ -168,16 +194,23 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                 acc = np.zeros((R, d))
                 for t0 in range(0, N, T):
                     t1 = min(N, t0 + T)
-                    if int8_qk:
+                    if int8_qk and qb > 1:
                         x = S[:, t0:t1]
                         c = (qf[:, None] * ks[None, t0:t1]).astype(F32)       # [R, t]
                         s = (x.astype(np.float64) * c).astype(F32)
+                    elif int8_qk:
+                        # per-token scales: the key scale first, the query factor last
+                        y = (S[:, t0:t1] * ks[None, t0:t1].astype(np.float64)).astype(F32)
+                        s = (y.astype(np.float64) * qf[:, None]).astype(F32)
                     else:
                         s = S[:, t0:t1].astype(F32)
                     m_new = np.maximum(m, s.max(axis=1))
                     nb = (LOG2_448_F32 - m_new).astype(F32)
-                    if int8_qk:
+                    if int8_qk and qb > 1:
                         arg = _fma_f32(x, c, np.broadcast_to(nb[:, None], x.shape))
+                    elif int8_qk:
+                        arg = _fma_f32(y, np.broadcast_to(qf[:, None], y.shape),
+                                       np.broadcast_to(nb[:, None], y.shape))
                     else:
                         arg = (s.astype(np.float64) + nb[:, None]).astype(F32)
                     p = _exp2_f32(arg)                                        # [R, t]

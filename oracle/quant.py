@@ -14,7 +14,9 @@ Readings of what the pages leave open (each also listed in the design notes):
   (round to nearest even), and is stored in bf16.  K' = fp32(K) - fp32(mean), one fp32
   subtraction per element.  Q and V are not smoothed.
 * INT8 granularity: one scale per (batch, head, block of 64 consecutive tokens), the
-  same for Q and K.  For a block, amax = max |x| over its valid rows;
+  same for Q and K.  A finer option gives every token its own scale (block = 1), the
+  per-token granularity that quality-first settings use (bjdmk page
+  "GitHub榜单静默期：Attention优化从架构转向推理加速", section 4.3).  For a block, amax = max |x| over its valid rows;
   scale = fp32(amax / 127); inv = fp32(127 / amax); code = clamp(rint(fp32(x * inv)),
   -127, 127) with rint rounding half to even.  The range is symmetric (-128 is never
   produced).  amax = 0 gives scale 0 and all-zero codes.  Scales do not contain the
@@ -108,7 +110,8 @@ def quantize_v_fp8(v):
 def quantize(q, k, v, smooth_k: bool = True, block: int = QUANT_BLOCK) -> dict:
     """All quantised operands of one attention call.  q, k, v: float32 [B, N, H, d]
     holding bf16 values.  ``smooth_k=False`` skips the K mean subtraction (used only to
-    measure what smoothing buys)."""
+    measure what smoothing buys).  ``block``: tokens per Q/K scale (64, or 1 for one
+    scale per token); it is returned with the operands."""
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     qh = q.transpose(0, 2, 1, 3)
@@ -123,4 +126,4 @@ def quantize(q, k, v, smooth_k: bool = True, block: int = QUANT_BLOCK) -> dict:
     k_i8, k_scale = quantize_int8_blocks(kr, block)
     v_f8, v_scale = quantize_v_fp8(v)
     return dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=mu,
-                v_f8=v_f8, v_scale=v_scale)
+                v_f8=v_f8, v_scale=v_scale, block=block)

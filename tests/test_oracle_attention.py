@@ -201,3 +201,66 @@ def test_quality_mode_error_budget():
     rq = oracle.rel_l2(_quality(q, k, v, kv_tile=128), ex)
     rs = oracle.rel_l2(attention_pipeline(q, k, v, kv_tile=128), ex)
     assert rq < 0.02 and rq < 0.6 * rs
+
+
+# ---- the fused multiply-add of the decision arithmetic ----
+
+def test_fma_is_single_rounding_against_exact_rationals():
+    from fractions import Fraction
+    from oracle.attention import _fma_f32
+
+    def rne_f32(fr):
+        # nearest fp32 to the exact rational, ties to the even pattern
+        c = np.float32(float(fr))
+        cands = [c, np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(-np.inf))]
+        return min(cands, key=lambda z: (abs(Fraction(float(z)) - fr),
+                                         int(np.array(z, np.float32).view(np.uint32)) & 1))
+
+    rng = np.random.default_rng(5)
+    x = rng.integers(-2 ** 23, 2 ** 23, 400).astype(np.float64)
+    c = (rng.standard_normal(400) * 1e-3).astype(np.float32)
+    b = (rng.standard_normal(400) * 10).astype(np.float32)
+    got = _fma_f32(x, c, b)
+    for i in range(400):
+        want = rne_f32(Fraction(float(x[i])) * Fraction(float(c[i])) + Fraction(float(b[i])))
+        assert got[i] == want
+    # sums that land exactly halfway between two fp32 values after fp64 rounding: the
+    # exact value decides (above, below, exact tie -> even)
+    xs = np.array([2.0 ** 6 + 2.0 ** -30, 2.0 ** 6 - 2.0 ** -30, 2.0 ** 6, -(2.0 ** 6 + 2.0 ** -30)])
+    bs = np.array([2.0 ** 30, 2.0 ** 30, 2.0 ** 30, -(2.0 ** 30)], np.float32)
+    got = _fma_f32(xs, np.ones(4, np.float32), bs).astype(np.float64)
+    assert list(got - np.array([2.0 ** 30, 2.0 ** 30, 2.0 ** 30, -(2.0 ** 30)])) == [128.0, 0.0, 0.0, -128.0]
+
+
+# ---- per-token INT8 scales ----
+
+def test_per_token_quality_mode_meets_the_rel_l2_gate():
+    # one INT8 scale per token for Q and K, with bf16 P.V: the configuration whose
+    # error stays under 0.01 of exact attention on the tiny workload
+    w = workloads.get("tiny")
+    q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+    ex = attention_exact(q, k, v)
+    r_tok = oracle.rel_l2(_quality(q, k, v, kv_tile=128, block=1), ex)
+    r_blk = oracle.rel_l2(_quality(q, k, v, kv_tile=128), ex)
+    assert r_tok <= 0.01 < r_blk
+
+
+def test_per_token_uniform_case_and_scales():
+    q, k, v = _qkv(1, 150, 2, 32, seed=23)
+    k[:] = k[:, :1]
+    quant = oracle.quantize(q, k, v, block=1)
+    assert quant["q_scale"].shape == (1, 2, 150) and quant["block"] == 1
+    o = _quality(q, k, v, kv_tile=64, quant=quant)
+    want = v.astype(np.float64).mean(axis=1)
+    assert np.abs(o - want[:, None]).max() < 1e-12 * max(1.0, np.abs(want).max())
+    # without fp8/bf16 rounding of P and V the per-token pipeline is the exact softmax
+    # of the dequantised operands
+    q2, k2, v2 = _qkv(1, 90, 1, 16, seed=24, kbias=2.0)
+    qt = oracle.quantize(q2, k2, v2, block=1)
+    got = attention_pipeline(q2, k2, v2, kv_tile=32, quant=qt, fp8_p=False, fp8_v=False)
+    qd = qt["q_i8"][0, 0].astype(np.float64) * qt["q_scale"][0, 0][:, None]
+    kd = qt["k_i8"][0, 0].astype(np.float64) * qt["k_scale"][0, 0][:, None]
+    s = qd @ kd.T / np.sqrt(16)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    want = (p / p.sum(axis=1, keepdims=True)) @ v2[0, :, 0, :].astype(np.float64)
+    assert np.abs(got[0, :, 0, :] - want).max() < 2e-5

@@ -70,13 +70,13 @@ def _rne(y: float) -> int:
     return f
 
 
-def _int8_bruteforce(x):
+def _int8_bruteforce(x, block=QUANT_BLOCK):
     """Scalar loops over blocks and elements (x: [N, d] float32 of one head)."""
     N, d = x.shape
     codes = np.zeros((N, d), np.int8)
     scales = []
-    for b0 in range(0, N, QUANT_BLOCK):
-        rows = range(b0, min(N, b0 + QUANT_BLOCK))
+    for b0 in range(0, N, block):
+        rows = range(b0, min(N, b0 + block))
         amax = F32(0)
         for i in rows:
             for c in range(d):
@@ -100,6 +100,21 @@ def test_int8_blocks_equal_scalar_loops(n):
         bc, bs = _int8_bruteforce(x[0, h])
         assert np.array_equal(codes[0, h], bc)
         assert np.array_equal(scales[0, h].view(np.uint32), bs.view(np.uint32))
+
+
+@pytest.mark.parametrize("n", [1, 5, 70])
+def test_int8_per_token_equals_scalar_loops(n):
+    # block = 1: every token row has its own scale
+    x = _bf16_values((1, 2, n, 16), seed=40 + n, scale=2.0)
+    codes, scales = quantize_int8_blocks(x, block=1)
+    assert scales.shape == (1, 2, n)
+    for h in range(2):
+        bc, bs = _int8_bruteforce(x[0, h], block=1)
+        assert np.array_equal(codes[0, h], bc)
+        assert np.array_equal(scales[0, h].view(np.uint32), bs.view(np.uint32))
+        rowmax = np.abs(x[0, h]) == np.abs(x[0, h]).max(axis=1, keepdims=True)
+        nz = np.abs(x[0, h]).max(axis=1) > 0
+        assert np.all(np.abs(codes[0, h][rowmax & nz[:, None]]) == 127)
 
 
 def test_int8_amax_element_maps_to_127_and_error_is_half_step():
