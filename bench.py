@@ -50,8 +50,9 @@ def quant_bytes(w) -> float:
     return 9.0 * E
 
 
-def measure_quality(w, steps, warmup):
-    """Whole-step time of the quality mode (INT8 Q.K^T, bf16 P.V) on workload w."""
+def measure_quality(w, steps, warmup, per_token=False):
+    """Whole-step time of the quality mode (INT8 Q.K^T, bf16 P.V; optionally per-token
+    Q/K scales) on workload w."""
     import torch
     import workloads
     import quantized_attention_diffusion_amd as sage
@@ -59,15 +60,16 @@ def measure_quality(w, steps, warmup):
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
     out = torch.empty_like(q)
-    ws = torch.empty(sage.sage_workspace_bytes_ex(w.B, w.H, w.N, w.d, "bf16"), dtype=torch.uint8, device=dev)
+    mode = sage.mode_bits("bf16", per_token)
+    ws = torch.empty(sage.sage_workspace_bytes_ex(w.B, w.H, w.N, w.d, mode), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16")
+        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16", per_token=per_token)
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
-        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16")
+        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16", per_token=per_token)
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
@@ -284,9 +286,10 @@ def main():
                            "quant_gbs": round(rs["quant_gbs"], 1)}
         for name in SWEEP + [w.name]:
             wq = workloads.get(name)
-            print(f"[bench] quality mode {name} N={wq.N}", file=sys.stderr, flush=True)
-            quality[name] = measure_quality(wq, args.steps if name == w.name else SWEEP_STEPS,
-                                            args.warmup if name == w.name else 2)
+            print(f"[bench] quality modes {name} N={wq.N}", file=sys.stderr, flush=True)
+            st, wu = (args.steps, args.warmup) if name == w.name else (SWEEP_STEPS, 2)
+            quality[name] = {"bf16_pv": measure_quality(wq, st, wu),
+                             "bf16_pv_per_token": measure_quality(wq, st, wu, per_token=True)}
     print(f"[bench] {w.name} B={w.B} H={w.H} N={w.N} d={w.d}: {args.warmup} warmup + {args.steps} steps",
           file=sys.stderr, flush=True)
     r = measure(w, args.steps, args.warmup)

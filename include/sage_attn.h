@@ -66,10 +66,11 @@ enum {
     SAGE_EHIP = -5             /* a kernel launch failed (HIP error text in sage_last_error) */
 };
 
-/* Precision of the P.V product (sage_attn_fwd_ex, sage_workspace_bytes_ex). */
+/* Mode bits of the _ex entry points; 0 is the default path of the others. */
 enum {
-    SAGE_PV_FP8 = 0,           /* speed: P and V in FP8 e4m3 (the default path) */
-    SAGE_PV_BF16 = 1           /* quality: P rounded to bf16, V unquantised bf16 */
+    SAGE_PV_FP8 = 0,           /* P and V in FP8 e4m3 (speed; the default) */
+    SAGE_PV_BF16 = 1,          /* P rounded to bf16, V unquantised bf16 (quality) */
+    SAGE_QK_PER_TOKEN = 2      /* one INT8 scale per Q and K token instead of per 64 */
 };
 
 typedef struct sage_info {
@@ -96,8 +97,8 @@ int64_t sage_padded_tokens(int N);
  * operands plus that scratch).  Status as for the calls they size. */
 int sage_quant_scratch_bytes(int B, int H, int N, int d, size_t* bytes);
 int sage_workspace_bytes(int B, int H, int N, int d, size_t* bytes);
-/* Workspace bytes of sage_attn_fwd_ex for pv_mode (SAGE_EINVAL for another mode). */
-int sage_workspace_bytes_ex(int B, int H, int N, int d, int pv_mode, size_t* bytes);
+/* Workspace bytes of sage_attn_fwd_ex for `mode` (SAGE_EINVAL for unknown bits). */
+int sage_workspace_bytes_ex(int B, int H, int N, int d, int mode, size_t* bytes);
 
 /*
  * sage_quant_qk - the quantisation pass.
@@ -119,6 +120,16 @@ int sage_quant_qk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                   uint16_t* k_mean, uint8_t* v_f8, float* v_scale,
                   void* scratch, size_t scratch_bytes, void* stream);
+
+/* sage_quant_qk with mode bits (see sage_attn_fwd_ex): SAGE_QK_PER_TOKEN gives per-token
+ * q_scale/k_scale [B][H][Npad]; SAGE_PV_BF16 writes bf16 V [B][H][d][Npad] into v_f8
+ * (sized 2 bytes per element) and leaves v_scale unwritten. */
+int sage_quant_qk_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const sage_strides* sq, const sage_strides* sk, const sage_strides* sv,
+                     int B, int H, int N, int d, int mode,
+                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                     uint16_t* k_mean, uint8_t* v_f8, float* v_scale,
+                     void* scratch, size_t scratch_bytes, void* stream);
 
 /*
  * sage_attn_fwd_prequant - fused attention on quantised operands.
@@ -151,24 +162,27 @@ int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
                   void* workspace, size_t workspace_bytes);
 
 /*
- * sage_attn_fwd_ex - sage_attn_fwd with a choice of P.V precision.  The pages note
- * that quantised attention schemes offer a quality-first setting beside the
- * speed-first one (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速",
- * section 4.3) and advise 16-bit attention for critical work (apatero page
+ * sage_attn_fwd_ex - sage_attn_fwd with quality options.  The pages note that
+ * quantised attention schemes offer a quality-first setting beside the speed-first
+ * one (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 4.3) and
+ * advise 16-bit attention for critical work (apatero page
  * "TeaCache和SageAttention优化实现更快的AI图像生成", section on when quality differences
- * appear).
- *   SAGE_PV_FP8:  identical to sage_attn_fwd.
- *   SAGE_PV_BF16: Q.K^T, k_mean, the scales and the softmax arithmetic are those of
- *     sage_attn_fwd (same p = 448 * 2^(s - m)); p is rounded to bf16 (nearest even)
- *     instead of e4m3, V is not quantised (its bf16 values, transposed to
- *     channel-major in the workspace), acc += P16 . V16 on bf16 matrix cores with fp32
- *     accumulation, O = acc / l.  The workspace (sage_workspace_bytes_ex) then holds
- *     bf16 V [B][H][d][Npad] in place of v_f8; v_scale is not written.
- * Any other pv_mode returns SAGE_EINVAL.
+ * appear).  `mode` is a combination of:
+ *   SAGE_PV_BF16: p (same p = 448 * 2^(s - m)) is rounded to bf16 (nearest even)
+ *     instead of e4m3 and V is not quantised (its bf16 values, transposed to
+ *     channel-major in the workspace); acc += P16 . V16 on bf16 matrix cores with fp32
+ *     accumulation, O = acc / l.  The workspace then holds bf16 V [B][H][d][Npad] in
+ *     place of v_f8; v_scale is not written.
+ *   SAGE_QK_PER_TOKEN: Q and K' are coded with one scale per token (amax over the
+ *     token's d channels; same rounding), q_scale/k_scale become [B][H][Npad].  The
+ *     logit arithmetic applies the key scale first: y = fp32(S * k_scale_j), the row
+ *     maximum is over fp32(y * qf), p = 448 * 2^(s - m) = exp2(fma(y, qf, log2(448) - m)).
+ * mode 0 is identical to sage_attn_fwd.  Unknown bits return SAGE_EINVAL.  The
+ * workspace size comes from sage_workspace_bytes_ex with the same mode.
  */
 int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                      int B, int H, int N, int d, float sm_scale,
-                     const sage_strides strides[4], int pv_mode, void* stream,
+                     const sage_strides strides[4], int mode, void* stream,
                      void* workspace, size_t workspace_bytes);
 
 /*

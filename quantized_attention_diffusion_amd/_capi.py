@@ -11,8 +11,8 @@ import torch
 __all__ = ["SageError", "lib_path", "load", "sage_last_error", "sage_kernel_info",
            "sage_padded_tokens", "sage_workspace_bytes", "sage_workspace_bytes_ex",
            "sage_quant_scratch_bytes", "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd",
-           "sage_attn_fwd_ex", "sage_debug_qk_i32", "sage_debug_e4m3", "EXPORTS", "STATUS",
-           "SAGE_PV_FP8", "SAGE_PV_BF16", "PV_MODES"]
+           "sage_attn_fwd_ex", "sage_quant_qk_ex", "sage_debug_qk_i32", "sage_debug_e4m3",
+           "EXPORTS", "STATUS", "SAGE_PV_FP8", "SAGE_PV_BF16", "SAGE_QK_PER_TOKEN", "mode_bits"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(HERE, "libsage_attn.so")
@@ -22,11 +22,18 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_EINVAL", -2: "SAGE_EUNSUPPORTED", -3: "SAGE_EA
 
 EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
            "sage_quant_scratch_bytes", "sage_workspace_bytes", "sage_workspace_bytes_ex",
-           "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd", "sage_attn_fwd_ex",
-           "sage_debug_qk_i32", "sage_debug_e4m3"]
+           "sage_quant_qk", "sage_quant_qk_ex", "sage_attn_fwd_prequant", "sage_attn_fwd",
+           "sage_attn_fwd_ex", "sage_debug_qk_i32", "sage_debug_e4m3"]
 
-SAGE_PV_FP8, SAGE_PV_BF16 = 0, 1
-PV_MODES = {"fp8": SAGE_PV_FP8, "bf16": SAGE_PV_BF16}
+SAGE_PV_FP8, SAGE_PV_BF16, SAGE_QK_PER_TOKEN = 0, 1, 2
+
+
+def mode_bits(pv: str = "fp8", per_token: bool = False) -> int:
+    """The C mode bits for P.V precision ``pv`` ('fp8' or 'bf16') and per-token Q/K
+    scales."""
+    if pv not in ("fp8", "bf16"):
+        raise ValueError(f"pv must be 'fp8' or 'bf16', got {pv!r}")
+    return (SAGE_PV_BF16 if pv == "bf16" else 0) | (SAGE_QK_PER_TOKEN if per_token else 0)
 
 
 class SageError(RuntimeError):
@@ -59,6 +66,9 @@ _SIGS = {
     "sage_quant_qk": (_I, [_P, _P, _P, ctypes.POINTER(sage_strides), ctypes.POINTER(sage_strides),
                            ctypes.POINTER(sage_strides), _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sage_quant_qk_ex": (_I, [_P, _P, _P, ctypes.POINTER(sage_strides), ctypes.POINTER(sage_strides),
+                              ctypes.POINTER(sage_strides), _I, _I, _I, _I, _I,
+                              _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sage_attn_fwd_prequant": (_I, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(sage_strides),
                                     _I, _I, _I, _I, ctypes.c_float, _P]),
     "sage_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
@@ -116,19 +126,10 @@ def sage_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return n.value
 
 
-def sage_workspace_bytes_ex(B: int, H: int, N: int, d: int, pv: str = "fp8") -> int:
+def sage_workspace_bytes_ex(B: int, H: int, N: int, d: int, mode: int = 0) -> int:
     n = _SZ()
-    _check(load().sage_workspace_bytes_ex(B, H, N, d, _pv(pv), ctypes.byref(n)))
+    _check(load().sage_workspace_bytes_ex(B, H, N, d, int(mode), ctypes.byref(n)))
     return n.value
-
-
-def _pv(pv) -> int:
-    """'fp8' / 'bf16' (or the SAGE_PV_* value) -> the C enum value."""
-    if isinstance(pv, str):
-        if pv not in PV_MODES:
-            raise ValueError(f"pv must be one of {sorted(PV_MODES)}, got {pv!r}")
-        return PV_MODES[pv]
-    return int(pv)
 
 
 def sage_quant_scratch_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -165,16 +166,17 @@ def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _alloc_quant(B, H, N, d, dev):
+def _alloc_quant(B, H, N, d, dev, mode=0):
     npad = sage_padded_tokens(N)
-    nblk = npad // 64
+    nsc = npad if mode & SAGE_QK_PER_TOKEN else npad // 64
+    vdt = torch.bfloat16 if mode & SAGE_PV_BF16 else torch.uint8
     return dict(
         q_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
-        q_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+        q_scale=torch.empty((B, H, nsc), dtype=torch.float32, device=dev),
         k_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
-        k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+        k_scale=torch.empty((B, H, nsc), dtype=torch.float32, device=dev),
         k_mean=torch.empty((B, H, d), dtype=torch.bfloat16, device=dev),
-        v_f8=torch.empty((B, H, d, npad), dtype=torch.uint8, device=dev),
+        v_f8=torch.empty((B, H, d, npad), dtype=vdt, device=dev),
         v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev),
     )
 
@@ -183,6 +185,13 @@ def sage_quant_qk(q, k, v, layout: str = "bnhd", out: dict | None = None,
                   scratch: torch.Tensor | None = None) -> dict:
     """Quantise Q, K, V (bf16 CUDA views in ``layout``).  Returns the dict of quantised
     operands (padded layouts of the C header) plus 'N'."""
+    return sage_quant_qk_ex(q, k, v, 0, layout=layout, out=out, scratch=scratch, _entry="sage_quant_qk")
+
+
+def sage_quant_qk_ex(q, k, v, mode: int, layout: str = "bnhd", out: dict | None = None,
+                     scratch: torch.Tensor | None = None, _entry: str = "sage_quant_qk_ex") -> dict:
+    """sage_quant_qk with mode bits (per-token scales, bf16 V).  The dict also holds
+    'mode'."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _bf16_cuda(n, t)
     (B, H, N, d), sq = _dims(q, layout)
@@ -191,16 +200,20 @@ def sage_quant_qk(q, k, v, layout: str = "bnhd", out: dict | None = None,
     if dk != (B, H, N, d) or dv != (B, H, N, d):
         raise ValueError("q, k and v must have the same shape")
     dev = q.device
-    o = out if out is not None else _alloc_quant(B, H, N, d, dev)
+    o = out if out is not None else _alloc_quant(B, H, N, d, dev, mode)
     if scratch is None:
         scratch = torch.empty(sage_quant_scratch_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
-    _check(load().sage_quant_qk(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sq), ctypes.byref(sk),
-        ctypes.byref(sv), B, H, N, d,
-        o["q_i8"].data_ptr(), o["q_scale"].data_ptr(), o["k_i8"].data_ptr(),
-        o["k_scale"].data_ptr(), o["k_mean"].data_ptr(), o["v_f8"].data_ptr(),
-        o["v_scale"].data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(dev)))
+    ptrs = (o["q_i8"].data_ptr(), o["q_scale"].data_ptr(), o["k_i8"].data_ptr(),
+            o["k_scale"].data_ptr(), o["k_mean"].data_ptr(), o["v_f8"].data_ptr(),
+            o["v_scale"].data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(dev))
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sq), ctypes.byref(sk),
+            ctypes.byref(sv), B, H, N, d)
+    if _entry == "sage_quant_qk":
+        _check(load().sage_quant_qk(*head, *ptrs))
+    else:
+        _check(load().sage_quant_qk_ex(*head, int(mode), *ptrs))
     o["N"] = N
+    o["mode"] = int(mode)
     return o
 
 
@@ -235,15 +248,17 @@ def sage_attn_fwd(q, k, v, out: torch.Tensor | None = None, sm_scale: float | No
     views in ``layout`` ('bnhd' = [B, N, H, d], 'bhnd' = [B, H, N, d]); any strides with
     a contiguous channel dimension (e.g. slices of a fused qkv tensor)."""
     return sage_attn_fwd_ex(q, k, v, out=out, sm_scale=sm_scale, layout=layout,
-                            workspace=workspace, pv="fp8", _entry="sage_attn_fwd")
+                            workspace=workspace, _entry="sage_attn_fwd")
 
 
 def sage_attn_fwd_ex(q, k, v, out: torch.Tensor | None = None, sm_scale: float | None = None,
                      layout: str = "bnhd", workspace: torch.Tensor | None = None,
-                     pv="fp8", _entry: str = "sage_attn_fwd_ex") -> torch.Tensor:
-    """sage_attn_fwd with the P.V precision ``pv``: 'fp8' (speed, the default path) or
-    'bf16' (quality: P rounded to bf16, V unquantised)."""
-    mode = _pv(pv)
+                     pv: str = "fp8", per_token: bool = False,
+                     _entry: str = "sage_attn_fwd_ex") -> torch.Tensor:
+    """sage_attn_fwd with quality options: ``pv`` = 'fp8' (speed, the default path) or
+    'bf16' (P rounded to bf16, V unquantised); ``per_token``: one INT8 scale per Q and
+    K token."""
+    mode = mode_bits(pv, per_token)
     for n, t in (("q", q), ("k", k), ("v", v)):
         _bf16_cuda(n, t)
     (B, H, N, d), sq = _dims(q, layout)

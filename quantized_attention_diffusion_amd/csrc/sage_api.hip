@@ -97,14 +97,16 @@ struct QuantLayout {
   size_t ksum, vmax, vinv;
 };
 
-// pv: the P.V mode; the quality mode's V region holds bf16 values (2 bytes each).
-QuantLayout layout(int B, int H, int N, int d, int pv = sage::kPvFp8) {
+// mode: SAGE_* bits.  With SAGE_PV_BF16 the V region holds bf16 values (2 bytes
+// each); with SAGE_QK_PER_TOKEN the Q/K scale arrays have one entry per token.
+QuantLayout layout(int B, int H, int N, int d, int mode = 0) {
   QuantLayout L;
   L.npad = sage::padded_tokens(N);
   const size_t bh = (size_t)B * H;
   L.q_i8 = L.k_i8 = bh * L.npad * d;
-  L.v_f8 = bh * L.npad * d * (pv == sage::kPvBf16 ? 2 : 1);
-  L.q_scale = L.k_scale = bh * (L.npad / sage::kQuantBlock) * sizeof(float);
+  L.v_f8 = bh * L.npad * d * ((mode & SAGE_PV_BF16) ? 2 : 1);
+  L.q_scale = L.k_scale =
+      bh * ((mode & SAGE_QK_PER_TOKEN) ? L.npad : L.npad / sage::kQuantBlock) * sizeof(float);
   L.k_mean = bh * d * sizeof(uint16_t);
   L.v_scale = bh * d * sizeof(float);
   const size_t chunks = sage::stats_chunks(N);
@@ -166,22 +168,22 @@ SAGE_EXPORT int sage_quant_scratch_bytes(int B, int H, int N, int d, size_t* byt
   return ok();
 }
 
-static int check_pv(int pv_mode) {
-  if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_BF16)
-    return fail(SAGE_EINVAL, "pv_mode %d is neither SAGE_PV_FP8 nor SAGE_PV_BF16", pv_mode);
+static int check_mode(int mode) {
+  if (mode & ~(SAGE_PV_BF16 | SAGE_QK_PER_TOKEN))
+    return fail(SAGE_EINVAL, "mode %#x has bits other than SAGE_PV_BF16 | SAGE_QK_PER_TOKEN", mode);
   return SAGE_OK;
 }
 
-SAGE_EXPORT int sage_workspace_bytes_ex(int B, int H, int N, int d, int pv_mode, size_t* bytes) {
+SAGE_EXPORT int sage_workspace_bytes_ex(int B, int H, int N, int d, int mode, size_t* bytes) {
   if (!bytes) return fail(SAGE_EINVAL, "bytes is NULL");
-  if (int rc = check_pv(pv_mode)) return rc;
+  if (int rc = check_mode(mode)) return rc;
   if (int rc = check_shape(B, H, N, d)) return rc;
-  *bytes = workspace_size(layout(B, H, N, d, pv_mode));
+  *bytes = workspace_size(layout(B, H, N, d, mode));
   return ok();
 }
 
 SAGE_EXPORT int sage_workspace_bytes(int B, int H, int N, int d, size_t* bytes) {
-  return sage_workspace_bytes_ex(B, H, N, d, SAGE_PV_FP8, bytes);
+  return sage_workspace_bytes_ex(B, H, N, d, 0, bytes);
 }
 
 static int validate_quant_inputs(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -194,16 +196,17 @@ static int validate_quant_inputs(const uint16_t* q, const uint16_t* k, const uin
   return SAGE_OK;
 }
 
-SAGE_EXPORT int sage_quant_qk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                              const sage_strides* sq, const sage_strides* sk, const sage_strides* sv,
-                              int B, int H, int N, int d,
-                              int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
-                              uint16_t* k_mean, uint8_t* v_f8, float* v_scale,
-                              void* scratch, size_t scratch_bytes, void* stream) {
+SAGE_EXPORT int sage_quant_qk_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const sage_strides* sq, const sage_strides* sk, const sage_strides* sv,
+                                 int B, int H, int N, int d, int mode,
+                                 int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                 uint16_t* k_mean, uint8_t* v_f8, float* v_scale,
+                                 void* scratch, size_t scratch_bytes, void* stream) {
+  if (int rc = check_mode(mode)) return rc;
   if (int rc = validate_quant_inputs(q, k, v, sq, sk, sv, B, H, N, d)) return rc;
   const void* outs[7] = {q_i8, q_scale, k_i8, k_scale, k_mean, v_f8, v_scale};
   const char* names[7] = {"q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_f8", "v_scale"};
-  const QuantLayout L = layout(B, H, N, d);
+  const QuantLayout L = layout(B, H, N, d, mode);
   const size_t sizes[7] = {L.q_i8, L.q_scale, L.k_i8, L.k_scale, L.k_mean, L.v_f8, L.v_scale};
   const Extent in[3] = {extent(q, *sq, B, H, N, d), extent(k, *sk, B, H, N, d), extent(v, *sv, B, H, N, d)};
   for (int i = 0; i < 7; ++i) {
@@ -227,10 +230,23 @@ SAGE_EXPORT int sage_quant_qk(const uint16_t* q, const uint16_t* k, const uint16
   a.sq = to_internal(*sq); a.sk = to_internal(*sk); a.sv = to_internal(*sv);
   a.B = B; a.H = H; a.N = N; a.d = d; a.npad = L.npad;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale;
-  a.k_mean = k_mean; a.v_f8 = v_f8; a.v_scale = v_scale; a.v16 = nullptr; a.pv = sage::kPvFp8;
+  a.k_mean = k_mean; a.v_f8 = v_f8; a.v_scale = v_scale;
+  a.pv = (mode & SAGE_PV_BF16) ? sage::kPvBf16 : sage::kPvFp8;
+  a.v16 = (mode & SAGE_PV_BF16) ? (uint16_t*)v_f8 : nullptr;
+  a.tok = (mode & SAGE_QK_PER_TOKEN) ? 1 : 0;
   char* p = (char*)scratch;
   carve_scratch(p, L, a);
   return launch_status(sage::launch_quant(a, (hipStream_t)stream), "quantisation");
+}
+
+SAGE_EXPORT int sage_quant_qk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const sage_strides* sq, const sage_strides* sk, const sage_strides* sv,
+                              int B, int H, int N, int d,
+                              int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                              uint16_t* k_mean, uint8_t* v_f8, float* v_scale,
+                              void* scratch, size_t scratch_bytes, void* stream) {
+  return sage_quant_qk_ex(q, k, v, sq, sk, sv, B, H, N, d, 0, q_i8, q_scale, k_i8, k_scale, k_mean,
+                          v_f8, v_scale, scratch, scratch_bytes, stream);
 }
 
 SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
@@ -258,7 +274,7 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
 
   sage::AttnArgs a;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale;
-  a.v_f8 = v_f8; a.v_scale = v_scale; a.v16 = nullptr; a.pv = sage::kPvFp8;
+  a.v_f8 = v_f8; a.v_scale = v_scale; a.v16 = nullptr; a.pv = sage::kPvFp8; a.tok = 0;
   a.out = out; a.so = to_internal(*so);
   a.B = B; a.H = H; a.N = N; a.d = d; a.npad = L.npad;
   a.log2e_scale = log2e_scale(sm_scale);
@@ -268,9 +284,9 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
 
 SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                                  int B, int H, int N, int d, float sm_scale,
-                                 const sage_strides strides[4], int pv_mode, void* stream,
+                                 const sage_strides strides[4], int mode, void* stream,
                                  void* workspace, size_t workspace_bytes) {
-  if (int rc = check_pv(pv_mode)) return rc;
+  if (int rc = check_mode(mode)) return rc;
   if (!strides) return fail(SAGE_EINVAL, "strides is NULL");
   if (int rc = validate_quant_inputs(q, k, v, &strides[0], &strides[1], &strides[2], B, H, N, d)) return rc;
   if (int rc = check_view("out", out, &strides[3], B, H, N, d)) return rc;
@@ -283,7 +299,7 @@ SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uin
       return fail(SAGE_EINVAL, "out overlaps %s", names[i]);
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale))
     return fail(SAGE_EINVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
-  const QuantLayout L = layout(B, H, N, d, pv_mode);
+  const QuantLayout L = layout(B, H, N, d, mode);
   const size_t need = workspace_size(L);
   if (!workspace) return fail(SAGE_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, kAlign)) return fail(SAGE_EWORKSPACE, "workspace is not 256-byte aligned");
@@ -307,15 +323,16 @@ SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uin
   qa.k_scale = (float*)p;  p += round_up(L.k_scale, kAlign);
   qa.k_mean = (uint16_t*)p; p += round_up(L.k_mean, kAlign);
   qa.v_scale = (float*)p;  p += round_up(L.v_scale, kAlign);
-  qa.pv = pv_mode;
-  qa.v16 = pv_mode == SAGE_PV_BF16 ? (uint16_t*)qa.v_f8 : nullptr;
+  qa.pv = (mode & SAGE_PV_BF16) ? sage::kPvBf16 : sage::kPvFp8;
+  qa.v16 = (mode & SAGE_PV_BF16) ? (uint16_t*)qa.v_f8 : nullptr;
+  qa.tok = (mode & SAGE_QK_PER_TOKEN) ? 1 : 0;
   carve_scratch(p, L, qa);
   hipStream_t s = (hipStream_t)stream;
   if (int rc = launch_status(sage::launch_quant(qa, s), "quantisation")) return rc;
 
   sage::AttnArgs a;
   a.q_i8 = qa.q_i8; a.q_scale = qa.q_scale; a.k_i8 = qa.k_i8; a.k_scale = qa.k_scale;
-  a.v_f8 = qa.v_f8; a.v_scale = qa.v_scale; a.v16 = qa.v16; a.pv = pv_mode;
+  a.v_f8 = qa.v_f8; a.v_scale = qa.v_scale; a.v16 = qa.v16; a.pv = qa.pv; a.tok = qa.tok;
   a.out = out; a.so = to_internal(strides[3]);
   a.B = B; a.H = H; a.N = N; a.d = d; a.npad = L.npad;
   a.log2e_scale = log2e_scale(sm_scale);
@@ -327,7 +344,7 @@ SAGE_EXPORT int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16
                               int B, int H, int N, int d, float sm_scale,
                               const sage_strides strides[4], void* stream,
                               void* workspace, size_t workspace_bytes) {
-  return sage_attn_fwd_ex(q, k, v, out, B, H, N, d, sm_scale, strides, SAGE_PV_FP8, stream,
+  return sage_attn_fwd_ex(q, k, v, out, B, H, N, d, sm_scale, strides, 0, stream,
                           workspace, workspace_bytes);
 }
 

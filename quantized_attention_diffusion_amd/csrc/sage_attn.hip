@@ -378,6 +378,79 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
   }
 }
 
+// Online-softmax update of both query groups with per-token scales: ks[kt][i] is the
+// scale of tile key 32g + 4kt + i and qf the query factor fp32(q_scale * sm_scale *
+// log2 e).  y = fp32(S * ks) per key; the row maximum is the max of fp32(y * qf) (qf >= 0
+// and rounding is monotone, so it is fp32(max y * qf)); p = exp2(fma(y, qf, nb)).  When
+// MASKED, keys at tile index >= nvalid get p = 0 and take no part in the maximum.
+template <int PV, bool MASKED>
+__device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const v4f (&ks)[8], const float (&qf)[G],
+                                                 int nvalid, int g, float log2_pscale, float (&m)[G],
+                                                 float (&lpart)[G], PTile<PV> (&P)[G], float (&alpha)[G]) {
+  float y[G][8][4];
+  float ym[G];
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) {
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[gq][kt][i] = (float)S[gq][kt][i] * ks[kt][i];
+    float a0 = -INFINITY, a1 = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 8; kt += 2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v0 = !MASKED || (4 * kt + i) < nvalid - 32 * g;
+        const bool v1 = !MASKED || (4 * kt + 4 + i) < nvalid - 32 * g;
+        a0 = fmaxf(a0, v0 ? y[gq][kt][i] : -INFINITY);
+        a1 = fmaxf(a1, v1 ? y[gq][kt + 1][i] : -INFINITY);
+      }
+    ym[gq] = fmaxf(a0, a1);
+  }
+  float nb[G], m_new[G];
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) {
+    const float sl = max_over_lane_groups(ym[gq] == -INFINITY ? -INFINITY : ym[gq] * qf[gq]);
+    m_new[gq] = fmaxf(m[gq], sl);
+    nb[gq] = log2_pscale - m_new[gq];
+    alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
+  }
+  float ls[G][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+#pragma unroll
+    for (int gq = 0; gq < G; ++gq) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[gq][kt][i], qf[gq], nb[gq]));
+        if constexpr (MASKED) p[i] = (4 * kt + i) < nvalid - 32 * g ? p[i] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
+      store_p<PV>(P[gq], kt, p);
+    }
+  }
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) {
+    lpart[gq] = alpha[gq] * lpart[gq] + ((ls[gq][0] + ls[gq][1]) + (ls[gq][2] + ls[gq][3]));
+    m[gq] = m_new[gq];
+  }
+}
+
+// Per-token key scales of one tile, staged in LDS next to the K tile: each wave copies
+// 128 of the 512 bytes with 8 lanes (one DMA instruction per wave).
+__device__ __forceinline__ void issue_kscale(const float* __restrict__ src, uint8_t* lds, int wave, int lane) {
+  if (lane < 8)
+    __builtin_amdgcn_global_load_lds(src + 32 * wave + 4 * lane, (lds_ptr_t)(lds + 128 * wave), 16, 0, 0);
+}
+
+// The lane's 32 key scales (keys 32g .. 32g+31) from the staged tile.
+__device__ __forceinline__ void load_kscale(const uint8_t* lds, int g, v4f (&ks)[8]) {
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) ks[kt] = *(const v4f*)(lds + 128 * g + 16 * kt);
+}
+
 // Maps the linear workgroup id to (head, query block) so that the workgroups one XCD
 // receives (ids x, x+8, x+16, ... go to XCD x) are consecutive query blocks of the same
 // heads and share that head's K/V tiles in the XCD's L2.
@@ -415,15 +488,21 @@ struct Ring {
   __device__ __forceinline__ uint8_t* vbuf(int t) const { return smem + (t % kStages) * STAGE + Lds<D>::KBYTES; }
 };
 
-template <int D, int PV>
+template <int D, int PV, bool TOK>
 struct AttnSmem {
-  static constexpr int BYTES = PV == kPvFp8 ? kStages * Ring<D>::STAGE
-                                            : 2 * Lds<D>::KBYTES + Lds<D>::V16BYTES;
+  static constexpr int MAIN = PV == kPvFp8 ? kStages * Ring<D>::STAGE
+                                           : 2 * Lds<D>::KBYTES + Lds<D>::V16BYTES;
+  static constexpr int KSCALE = TOK ? 2 * 512 : 0;   // per-token key scales, 2 buffers
+  static constexpr int BYTES = MAIN + KSCALE;
 };
 
-template <int D, int PV>
+// TOK: per-token Q/K scales (q_scale, k_scale [B][H][Npad]); the key scales of each
+// tile are staged in LDS with the K tile.
+template <int D, int PV, bool TOK>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[AttnSmem<D, PV>::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[AttnSmem<D, PV, TOK>::BYTES];
+  uint8_t* const ksmem = smem + AttnSmem<D, PV, TOK>::MAIN;
+  auto ksbuf = [&](int t) { return ksmem + (t & 1) * 512; };
 
   // workgroup-uniform indices kept in scalar registers (readfirstlane), so that the
   // per-tile k_scale reads are scalar loads and never wait on the vector-memory counter
@@ -450,6 +529,9 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 
   float qf[G], m[G], lpart[G], alpha[G], c[G];
   v4f acc[G][D / 16];
+  v4i qfr[G][D / 64];
+  v4i S[G][8];
+  PTile<PV> P[G];
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef const __attribute__((address_space(4))) f32x2* const_f32x2_ptr;
   auto scale_products = [&](int t) {
@@ -459,19 +541,41 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) c[gq] = qf[gq] * ks;
   };
+  const float* kscale_h = a.k_scale + bh * a.npad;   // per-token key scales of the head
+  auto copy_ks = [&](int t) {
+    if constexpr (TOK) {
+      if (t < ntiles) issue_kscale(kscale_h + (int64_t)t * kKvTile, ksbuf(t), wave, lane);
+    }
+  };
+  // softmax of tile t, masked to `tail` keys or not
+  auto softmax_step = [&](int t, bool masked) {
+    if constexpr (TOK) {
+      v4f ks[8];
+      load_kscale(ksbuf(t), g, ks);
+      if (!masked) softmax_tile_tok<PV, false>(S, ks, qf, kKvTile, g, a.log2_pscale, m, lpart, P, alpha);
+      else softmax_tile_tok<PV, true>(S, ks, qf, tail, g, a.log2_pscale, m, lpart, P, alpha);
+    } else {
+      scale_products(t);
+      if (!masked) {
+        softmax_tile<PV>(S, c, a.log2_pscale, m, lpart, P, alpha);
+      } else {
+#pragma unroll
+        for (int gq = 0; gq < G; ++gq)
+          alpha[gq] = softmax_group<true, PV>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
+      }
+    }
+  };
   auto init_state = [&]() {
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
-      qf[gq] = a.q_scale[bh * nblk + (qrow0 + 16 * gq) / kQuantBlock] * a.log2e_scale;
+      qf[gq] = (TOK ? a.q_scale[bh * a.npad + qrow0 + 16 * gq + r]
+                    : a.q_scale[bh * nblk + (qrow0 + 16 * gq) / kQuantBlock]) * a.log2e_scale;
       m[gq] = -INFINITY;
       lpart[gq] = 0.0f;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) acc[gq][dt] = v4f{0.f, 0.f, 0.f, 0.f};
     }
   };
-  v4i qfr[G][D / 64];
-  v4i S[G][8];
-  PTile<PV> P[G];
 
   if constexpr (PV == kPvFp8) {
     const Ring<D> ring{smem};
@@ -480,34 +584,31 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
       if (t < ntiles) {
         dma.issue_k(kh + (int64_t)t * kKvTile * D, ring.kbuf(t), wave);
         dma.issue_v(vh + (int64_t)t * kKvTile, ring.vbuf(t), wave);
+        copy_ks(t);
       }
     };
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t) copy_tile(t);
     load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
     init_state();
-    constexpr int KEEP = (kStages - 2) * DmaOffsets<D>::PER_TILE;
+    constexpr int KEEP = (kStages - 2) * (DmaOffsets<D>::PER_TILE + (TOK ? 1 : 0));
     for (int t = 0; t < nfull; ++t) {
       // tile t has landed once only the copies of the kStages-2 later tiles may be in flight
       if (t + kStages - 2 < ntiles) tile_barrier<KEEP>();
       else tile_barrier<0>();
       copy_tile(t + kStages - 1);        // into the stage all waves finished in step t-1
-      scale_products(t);
       qk_tile<D>(ring.kbuf(t), qfr, lo, S);
-      softmax_tile<PV>(S, c, a.log2_pscale, m, lpart, P, alpha);
+      softmax_step(t, false);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
       pv_tile<D>(ring.vbuf(t), P, lo, acc);
     }
     if (nfull < ntiles) {                // last tile: keys >= N masked
       tile_barrier<0>();
-      scale_products(nfull);
       qk_tile<D>(ring.kbuf(nfull), qfr, lo, S);
+      softmax_step(nfull, true);
 #pragma unroll
-      for (int gq = 0; gq < G; ++gq) {
-        alpha[gq] = softmax_group<true, PV>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
-        rescale<D>(acc[gq], alpha[gq]);
-      }
+      for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
       pv_tile<D>(ring.vbuf(nfull), P, lo, acc);
     }
   } else {
@@ -520,7 +621,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
     const DmaOffsets16<D> dma16(wave, lane, a.npad);
     const uint8_t* vh = (const uint8_t*)(a.v16 + bh * D * a.npad);
     auto copy_k = [&](int t) {
-      if (t < ntiles) dma.issue_k(kh + (int64_t)t * kKvTile * D, kbuf(t), wave);
+      if (t < ntiles) {
+        dma.issue_k(kh + (int64_t)t * kKvTile * D, kbuf(t), wave);
+        copy_ks(t);
+      }
     };
     copy_k(0);
     load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
@@ -529,18 +633,12 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
       tile_barrier<0>();
       dma16.issue_v(vh + (int64_t)t * kKvTile * 2, vbuf, wave);
       copy_k(t + 1);
-      scale_products(t);
       qk_tile<D>(kbuf(t), qfr, lo, S);
-      if (!masked) {
-        softmax_tile<PV>(S, c, a.log2_pscale, m, lpart, P, alpha);
-      } else {
-#pragma unroll
-        for (int gq = 0; gq < G; ++gq)
-          alpha[gq] = softmax_group<true, PV>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
-      }
+      softmax_step(t, masked);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
-      if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW>();
+      // V(t) must have landed; the copies of tile t+1 (K and key scales) may be in flight
+      if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW + (TOK ? 1 : 0)>();
       else tile_barrier<0>();
       pv_tile16<D>(vbuf, P, lo16, acc);
     };
@@ -605,20 +703,25 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
   }
 }
 
+template <int D, int PV>
+static void launch_attn_tok(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if (a.tok)
+    hipLaunchKernelGGL((k_attn<D, PV, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn<D, PV, false>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
+template <int D>
+static void launch_attn_d(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if (a.pv == kPvBf16) launch_attn_tok<D, kPvBf16>(a, grid, s);
+  else launch_attn_tok<D, kPvFp8>(a, grid, s);
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int nqb = (int)(a.npad / kBlockM);
   const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.H);
-  if (a.pv == kPvBf16) {
-    if (a.d == 64)
-      hipLaunchKernelGGL((k_attn<64, kPvBf16>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_attn<128, kPvBf16>), dim3(grid), dim3(kThreads), 0, s, a);
-  } else {
-    if (a.d == 64)
-      hipLaunchKernelGGL((k_attn<64, kPvFp8>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_attn<128, kPvFp8>), dim3(grid), dim3(kThreads), 0, s, a);
-  }
+  if (a.d == 64) launch_attn_d<64>(a, grid, s);
+  else launch_attn_d<128>(a, grid, s);
   return hipGetLastError();
 }
 
@@ -637,10 +740,14 @@ hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_
 
 // explicit instantiations: the host pass does not always emit launch stubs for kernel
 // templates that are only named inside hipLaunchKernelGGL
-template __global__ void k_attn<64, kPvFp8>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8>(AttnArgs);
-template __global__ void k_attn<64, kPvBf16>(AttnArgs);
-template __global__ void k_attn<128, kPvBf16>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, false>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, true>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, true>(AttnArgs);
 template __global__ void k_debug_qk<64>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,
                                         int64_t, int, int, int, int32_t* __restrict__);
 template __global__ void k_debug_qk<128>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,

@@ -54,6 +54,7 @@ struct QuantArgs {
   float* v_scale;
   uint16_t* v16;       // kPvBf16: bf16 V [B][H][d][Npad]
   int pv;              // PvMode
+  int tok;             // 1: Q/K scales per token [B][H][Npad], 0: per 64-token block
   double* ksum_part;   // [B*H][chunks][d]
   float* vmax_part;    // [B*H][chunks][d]
   float* v_inv;        // [B*H][d]
@@ -69,6 +70,7 @@ struct AttnArgs {
   const float* v_scale;
   const uint16_t* v16;
   int pv;              // PvMode
+  int tok;             // Q/K scales per token
   uint16_t* out;
   Strides so;
   int B, H, N, d;

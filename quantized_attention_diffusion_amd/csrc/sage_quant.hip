@@ -3,7 +3,7 @@
 // SageAttention 实测加速", section 一; the bf16 mean term of the sd114.wiki
 // ComfyUI-sol-attn page, "核心亮点" item 1).
 //
-// Three launches, all HBM-bound:
+// Three launches, all HBM-bound (Q/K scales per 64-token block, or per token):
 //   1. q+stats  grid (chunks, H, B): each workgroup walks a run of 64-token blocks; it
 //               writes the final INT8 codes and scales of Q (they need only the block
 //               itself) and one row of fp64 partial sums of K and partial max |V| per
@@ -47,6 +47,31 @@ __device__ __forceinline__ float int8_block(const float (&x)[RPT][8], uint2 (&co
   return amax / 127.0f;
 }
 
+// Per-token INT8 codes: row i of x is one token, held by the TPR consecutive lanes that
+// share it (8 channels each); its max |x| is reduced over those lanes.  Returns the
+// scales of the thread's RPT rows.
+template <int RPT, int TPR>
+__device__ __forceinline__ void int8_rows(const float (&x)[RPT][8], uint2 (&codes)[RPT], float (&scale)[RPT]) {
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[i][j]));
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float y = rintf(x[i][j] * inv);                // round half to even
+      y = fminf(fmaxf(y, -127.0f), 127.0f);
+      w[j >> 2] |= ((uint32_t)((int)y & 0xff)) << (8 * (j & 3));
+    }
+    codes[i] = make_uint2(w[0], w[1]);
+    scale[i] = amax / 127.0f;
+  }
+}
+
 // Loads the 16-byte words (8 channels) of rows row0 + r + RPI*i of one 64-token block;
 // rows at or past N read as zero.
 template <int RPT, int RPI>
@@ -62,7 +87,8 @@ __device__ __forceinline__ void load_block(const uint16_t* base, int64_t stride_
 
 // NEED_V: the speed mode also needs the per-channel max |V| (e4m3 V scales); the
 // quality mode keeps V in bf16 and skips it.
-template <int D, bool NEED_V>
+// TOK: one INT8 scale per token (q_scale [B][H][Npad]) instead of per 64-token block.
+template <int D, bool NEED_V, bool TOK>
 __global__ __launch_bounds__(256) void k_quant_q_stats(
     const uint16_t* __restrict__ q, Strides sq, const uint16_t* __restrict__ k, Strides sk,
     const uint16_t* __restrict__ v, Strides sv, int H, int N, int64_t npad, int blocks_per_chunk,
@@ -98,11 +124,19 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
     uint2 codes[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) bf16x8_to_f32(qw[i], x[i]);
-    const float scale = int8_block<RPT>(x, codes, red);
+    if constexpr (TOK) {
+      float sc[RPT];
+      int8_rows<RPT, TPR>(x, codes, sc);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        if (cg == 0) q_scale[bh * npad + row0 + r + RPI * i] = sc[i];
+    } else {
+      const float scale = int8_block<RPT>(x, codes, red);
+      if (t == 0) q_scale[bh * nblk + blk] = scale;
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       *(uint2*)(q_i8 + (bh * npad + row0 + r + RPI * i) * D + 8 * cg) = codes[i];
-    if (t == 0) q_scale[bh * nblk + blk] = scale;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       float kx[8];
@@ -173,7 +207,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
 //
 // V16 (quality mode): V keeps its bf16 values and is only transposed: each thread's
 // RPT tokens of a channel (2*RPT bytes) go to LDS as RPT/2 words in rows of 33 words.
-template <int D, bool V16>
+template <int D, bool V16, bool TOK>
 __global__ __launch_bounds__(256) void k_quant_kv(
     const uint16_t* __restrict__ k, Strides sk, const uint16_t* __restrict__ v, Strides sv,
     int H, int N, int64_t npad, const uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
@@ -214,11 +248,19 @@ __global__ __launch_bounds__(256) void k_quant_kv(
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[i][j] = valid ? x[i][j] - mu[j] : 0.0f;
     }
-    const float scale = int8_block<RPT>(x, codes, red);
+    if constexpr (TOK) {
+      float sc[RPT];
+      int8_rows<RPT, TPR>(x, codes, sc);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        if (cg == 0) k_scale[bh * npad + tok0 + i] = sc[i];
+    } else {
+      const float scale = int8_block<RPT>(x, codes, red);
+      if (t == 0) k_scale[bh * nblk + blk] = scale;
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       *(uint2*)(k_i8 + (bh * npad + tok0 + i) * D + 8 * cg) = codes[i];
-    if (t == 0) k_scale[bh * nblk + blk] = scale;
   }
   if constexpr (V16) {
     // ---- V (bf16) transposed to [channel][token] ----
@@ -291,24 +333,29 @@ __global__ void k_debug_e4m3(const float* __restrict__ x, uint8_t* __restrict__ 
   }
 }
 
-template <int D, bool V16>
+template <int D, bool V16, bool TOK>
 static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   const int per = stats_blocks_per_chunk(a.npad);
   const int chunks = stats_chunks(a.N);
-  hipLaunchKernelGGL((k_quant_q_stats<D, !V16>), dim3(chunks, a.H, a.B), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_quant_q_stats<D, !V16, TOK>), dim3(chunks, a.H, a.B), dim3(256), 0, s,
                      a.q, a.sq, a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, per,
                      a.q_i8, a.q_scale, a.ksum_part, a.vmax_part);
   hipLaunchKernelGGL((k_quant_finalize<D, !V16>), dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
                      a.ksum_part, a.vmax_part, chunks, a.N, a.k_mean, a.v_scale, a.v_inv);
-  hipLaunchKernelGGL((k_quant_kv<D, V16>), dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_quant_kv<D, V16, TOK>), dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
                      a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, a.k_mean, a.v_inv,
                      a.k_i8, a.k_scale, a.v_f8, a.v16);
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_quant_mode(const QuantArgs& a, hipStream_t s) {
+  if (a.pv == kPvBf16) return a.tok ? launch_quant_d<D, true, true>(a, s) : launch_quant_d<D, true, false>(a, s);
+  return a.tok ? launch_quant_d<D, false, true>(a, s) : launch_quant_d<D, false, false>(a, s);
+}
+
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
-  if (a.pv == kPvBf16) return a.d == 64 ? launch_quant_d<64, true>(a, s) : launch_quant_d<128, true>(a, s);
-  return a.d == 64 ? launch_quant_d<64, false>(a, s) : launch_quant_d<128, false>(a, s);
+  return a.d == 64 ? launch_quant_mode<64>(a, s) : launch_quant_mode<128>(a, s);
 }
 
 hipError_t launch_debug_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t s) {

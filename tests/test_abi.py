@@ -122,26 +122,33 @@ def test_quant_and_debug_entry_points_validate(lib):
     assert rc == -1 and "sm_scale" in _err(lib)
 
 
-def test_pv_mode_entry_points_validate(lib):
+def test_mode_entry_points_validate(lib):
     from quantized_attention_diffusion_amd import _capi
     from quantized_attention_diffusion_amd._capi import sage_strides
     B, H, N, d = 1, 24, 4608, 128
-    fp8 = _capi.sage_workspace_bytes_ex(B, H, N, d, "fp8")
-    bf16 = _capi.sage_workspace_bytes_ex(B, H, N, d, "bf16")
-    assert fp8 == _capi.sage_workspace_bytes(B, H, N, d)
-    assert bf16 - fp8 == B * H * N * d                  # the V region holds 2-byte values
+    base = _capi.sage_workspace_bytes_ex(B, H, N, d, 0)
+    bf16 = _capi.sage_workspace_bytes_ex(B, H, N, d, _capi.mode_bits("bf16"))
+    tok = _capi.sage_workspace_bytes_ex(B, H, N, d, _capi.mode_bits("fp8", per_token=True))
+    assert base == _capi.sage_workspace_bytes(B, H, N, d)
+    assert bf16 - base == B * H * N * d                  # the V region holds 2-byte values
+    assert tok - base == 2 * 4 * B * H * (N - N // 64)   # two scale arrays grow to one per token
     n = ctypes.c_size_t()
-    assert lib.sage_workspace_bytes_ex(B, H, N, d, 7, ctypes.byref(n)) == -1 and "pv_mode" in _err(lib)
+    assert lib.sage_workspace_bytes_ex(B, H, N, d, 4, ctypes.byref(n)) == -1 and "mode" in _err(lib)
     st = (sage_strides * 4)(*([_st(100 * 2 * 128, 128, 2 * 128)] * 4))
-    # an unknown mode is rejected before anything else
-    rc = lib.sage_attn_fwd_ex(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 2, None, W, 1 << 40)
-    assert rc == -1 and "pv_mode" in _err(lib)
+    # unknown mode bits are rejected before anything else
+    rc = lib.sage_attn_fwd_ex(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 8, None, W, 1 << 40)
+    assert rc == -1 and "mode" in _err(lib)
     # the quality mode needs its larger workspace
     lib.sage_workspace_bytes_ex(1, 2, 100, 128, 0, ctypes.byref(n))
     rc = lib.sage_attn_fwd_ex(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 1, None, W, n.value)
     assert rc == -4 and "needed" in _err(lib)
-    rc = lib.sage_attn_fwd_ex(0, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 1, None, W, 1 << 40)
+    rc = lib.sage_attn_fwd_ex(0, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 3, None, W, 1 << 40)
     assert rc == -1 and "q is NULL" in _err(lib)
+    s1 = _st(100 * 2 * 64, 64, 2 * 64)
+    rc = lib.sage_quant_qk_ex(A, B_, C, ctypes.byref(s1), ctypes.byref(s1), ctypes.byref(s1),
+                              1, 2, 100, 64, 16, O, O + (1 << 20), O + (2 << 20), O + (3 << 20),
+                              O + (4 << 20), O + (5 << 20), O + (6 << 20), W, 1 << 20, None)
+    assert rc == -1 and "mode" in _err(lib)
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -208,3 +208,51 @@ def test_quality_mode_layouts_degenerate_and_fp8_entry():
     k2[:] = k2[:, :1]
     o2 = sage.sage_attn_fwd_ex(q.cuda(), k2.cuda(), v.cuda(), pv="bf16")
     check_attention(to_np(o2), _quality_pipe(q, k2, v), "quality uniform")
+
+
+
+# ---- per-token Q/K scales (with FP8 or bf16 P.V) ----
+
+def _head_slice(d, b, h):
+    return {k: (v[b:b + 1, h:h + 1] if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("pv", ["fp8", "bf16"])
+@pytest.mark.parametrize("case", CASES[:6] + CASES[7:9], ids=_case_id)
+def test_per_token_mode_matches_oracle(case, pv):
+    B, N, H, d, seed, outl = case
+    print(f"[per-token {pv}] {_case_id(case)}", flush=True)
+    q, k, v = random_qkv(B, N, H, d, seed, outl)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    mode = sage.mode_bits(pv, per_token=True)
+    ref = oracle.quantize(_np(q), _np(k), _np(v), block=1)
+    # per-token codes and scales bit-exact
+    gq = sage.sage_quant_qk_ex(qc, kc, vc, mode)
+    torch.cuda.synchronize()
+    for name in ("q", "k"):
+        codes = gq[f"{name}_i8"].cpu().numpy()
+        assert np.array_equal(codes[:, :, :N], ref[f"{name}_i8"]), f"{name}_i8 differs"
+        assert not codes[:, :, N:].any()
+        sc = gq[f"{name}_scale"].cpu().numpy()
+        assert np.array_equal(sc[:, :, :N].view(np.uint32), ref[f"{name}_scale"].view(np.uint32)), f"{name}_scale differs"
+        assert not sc[:, :, N:].any()
+    if pv == "bf16":
+        # V is transposed, not quantised
+        v16 = gq["v_f8"].float().cpu().numpy().transpose(0, 1, 3, 2)
+        assert np.array_equal(v16[:, :, :N], _np(v).transpose(0, 2, 1, 3)) and not v16[:, :, N:].any()
+    out = sage.sage_attn_fwd_ex(qc, kc, vc, pv=pv, per_token=True)
+    o = to_np(out)
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE, quant=ref,
+                                     fp8_p=(pv == "fp8"), bf16_p=(pv == "bf16"), fp8_v=(pv == "fp8"))
+    err = check_attention(o, pipe, f"per-token {pv} " + _case_id(case))
+    exact = oracle.attention_exact(_np(q), _np(k), _np(v))
+    assert oracle.rel_l2(o, exact) <= oracle.rel_l2(pipe, exact) + 0.002
+    print(f"    max|gpu-pipe| = {err:.2e}  relL2(gpu, exact) = {oracle.rel_l2(o, exact):.4f}", flush=True)
+
+
+def test_per_token_quality_mode_meets_rel_l2_gate_on_tiny():
+    w = workloads.get("tiny")
+    q, k, v = workloads.make_qkv(w)
+    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16", per_token=True)
+    exact = oracle.attention_exact(_np(q), _np(k), _np(v))
+    assert oracle.rel_l2(to_np(out), exact) <= 0.01
