@@ -86,12 +86,13 @@ def test_full_size_parity(name):
         assert r_gpu <= r_pipe + 0.002
 
 
+@pytest.mark.parametrize("per_token", [False, True], ids=["block64", "per_token"])
 @pytest.mark.parametrize("name", ["flux_like", "video"])
-def test_full_size_quality_mode(name):
+def test_full_size_quality_mode(name, per_token):
     w = workloads.get(name)
-    print(f"[full quality] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
+    print(f"[full quality] {name} B={w.B} H={w.H} N={w.N} d={w.d} per_token={per_token}", flush=True)
     q, k, v = workloads.make_qkv(w)
-    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16")
+    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16", per_token=per_token)
     torch.cuda.synchronize()
     rng = np.random.default_rng(4321)
     N = w.N
@@ -99,7 +100,7 @@ def test_full_size_quality_mode(name):
         qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=N_ROWS, replace=False)]))
         pipe = oracle.attention_pipeline(qh, kh, vh, kv_tile=128, rows=rows, fp8_p=False,
-                                         bf16_p=True, fp8_v=False)
+                                         bf16_p=True, fp8_v=False, block=1 if per_token else 64)
         o = to_np(out[:, rows, h:h + 1, :])
         err = check_attention(o, pipe, f"{name} quality head {h}")
         exact = oracle.attention_exact(qh, kh, vh, rows=rows)
