@@ -11,7 +11,8 @@
 //   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 2 groups of 16
 //   queries; 2 workgroups per CU (2 waves per SIMD).  Keys are visited in tiles of 128.
 //   K tiles (128 x d int8) and V tiles (d x 128, channel-major) are copied HBM -> LDS
-//   by LDS DMA (global_load_lds_dwordx4, no registers involved) and shared by the 4
+//   by LDS DMA (buffer_load_dwordx4 ... lds: no data registers, and the per-tile
+//   address advance is a scalar offset, so no vector instruction) and shared by the 4
 //   waves: speed mode double-buffers (K, V) stages, one tile ahead of use; quality mode
 //   double-buffers K and refills a single bf16 V buffer while S and the softmax of the
 //   same tile are computed.  Waits are counted (s_waitcnt vmcnt(n) + s_barrier), so a
@@ -94,10 +95,15 @@ struct LaneOffsets {
   }
 };
 
+// Buffer resource of `bytes` bytes at p (raw buffer, no stride; gfx9 descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // Per-lane source offsets of the LDS DMA copies (computed once per kernel): the K tile
 // copy of wave w, instruction j reads K + koff[j], the V tile copy V + voff[j] (bytes,
 // relative to the tile's first key), which lands at LDS offset (w*PW + j)*1024 + 16*lane:
-// global_load_lds_dwordx4 writes lane i's 16 bytes at 16*i of the instruction's 1 KB, so
+// buffer_load_dwordx4 ... lds writes lane i's 16 bytes at 16*i of the instruction's 1 KB, so
 // the swizzle is applied by choosing which global chunk lane i reads.
 template <int D>
 struct DmaOffsets {
@@ -120,15 +126,18 @@ struct DmaOffsets {
       voff[j] = (uint32_t)(ch * npad + (pc ^ vswz(ch)) * 16);
     }
   }
-  __device__ __forceinline__ void issue_k(const int8_t* __restrict__ ktile, uint8_t* klds, int wave) const {
+  // tile_off: byte offset of the tile inside the buffer (a scalar operand)
+  __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t kbufr, int tile_off, uint8_t* klds, int wave) const {
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
-      __builtin_amdgcn_global_load_lds(ktile + koff[j], (lds_ptr_t)(klds + (wave * KPW + j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kbufr, (lds_ptr_t)(klds + (wave * KPW + j) * 1024), 16, koff[j],
+                                               tile_off, 0, 0);
   }
-  __device__ __forceinline__ void issue_v(const uint8_t* __restrict__ vtile, uint8_t* vlds, int wave) const {
+  __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t vbufr, int tile_off, uint8_t* vlds, int wave) const {
 #pragma unroll
     for (int j = 0; j < VPW; ++j)
-      __builtin_amdgcn_global_load_lds(vtile + voff[j], (lds_ptr_t)(vlds + (wave * VPW + j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vbufr, (lds_ptr_t)(vlds + (wave * VPW + j) * 1024), 16, voff[j],
+                                               tile_off, 0, 0);
   }
 };
 
@@ -156,10 +165,11 @@ struct DmaOffsets16 {
       voff[j] = (uint32_t)(ch * npad * 2 + (pc ^ v16swz(ch & 15)) * 16);
     }
   }
-  __device__ __forceinline__ void issue_v(const uint8_t* __restrict__ vtile, uint8_t* vlds, int wave) const {
+  __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t vbufr, int tile_off, uint8_t* vlds, int wave) const {
 #pragma unroll
     for (int j = 0; j < VPW; ++j)
-      __builtin_amdgcn_global_load_lds(vtile + voff[j], (lds_ptr_t)(vlds + (wave * VPW + j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vbufr, (lds_ptr_t)(vlds + (wave * VPW + j) * 1024), 16, voff[j],
+                                               tile_off, 0, 0);
   }
 };
 
@@ -440,9 +450,10 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const v4f (&ks)
 
 // Per-token key scales of one tile, staged in LDS next to the K tile: each wave copies
 // 128 of the 512 bytes with 8 lanes (one DMA instruction per wave).
-__device__ __forceinline__ void issue_kscale(const float* __restrict__ src, uint8_t* lds, int wave, int lane) {
+__device__ __forceinline__ void issue_kscale(__amdgpu_buffer_rsrc_t ksr, int tile_off, uint8_t* lds, int wave, int lane) {
   if (lane < 8)
-    __builtin_amdgcn_global_load_lds(src + 32 * wave + 4 * lane, (lds_ptr_t)(lds + 128 * wave), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksr, (lds_ptr_t)(lds + 128 * wave), 16, 128 * wave + 16 * lane,
+                                             tile_off, 0, 0);
 }
 
 // The lane's 32 key scales (keys 32g .. 32g+31) from the staged tile.
@@ -520,6 +531,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
   const LaneOffsets<D> lo(lane);
   const DmaOffsets<D> dma(wave, lane, a.npad);
   const int8_t* kh = a.k_i8 + bh * a.npad * D;
+  // buffer resources of this head's operands (byte ranges; reads past them return 0)
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kh, a.npad * D);
   typedef const __attribute__((address_space(4))) float* const_f32_ptr;
   // k_scale through the constant address space: scalar loads (counted by lgkmcnt)
   const const_f32_ptr ksh = (const_f32_ptr)(a.k_scale + bh * nblk);
@@ -541,10 +554,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) c[gq] = qf[gq] * ks;
   };
-  const float* kscale_h = a.k_scale + bh * a.npad;   // per-token key scales of the head
+  const __amdgpu_buffer_rsrc_t ks_rsrc = make_rsrc(a.k_scale + bh * a.npad, TOK ? a.npad * 4 : 0);
   auto copy_ks = [&](int t) {
     if constexpr (TOK) {
-      if (t < ntiles) issue_kscale(kscale_h + (int64_t)t * kKvTile, ksbuf(t), wave, lane);
+      if (t < ntiles) issue_kscale(ks_rsrc, t * kKvTile * 4, ksbuf(t), wave, lane);
     }
   };
   // softmax of tile t, masked to `tail` keys or not
@@ -579,11 +592,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 
   if constexpr (PV == kPvFp8) {
     const Ring<D> ring{smem};
-    const uint8_t* vh = a.v_f8 + bh * D * a.npad;
+    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(a.v_f8 + bh * D * a.npad, (int64_t)D * a.npad);
     auto copy_tile = [&](int t) {
       if (t < ntiles) {
-        dma.issue_k(kh + (int64_t)t * kKvTile * D, ring.kbuf(t), wave);
-        dma.issue_v(vh + (int64_t)t * kKvTile, ring.vbuf(t), wave);
+        dma.issue_k(k_rsrc, t * kKvTile * D, ring.kbuf(t), wave);
+        dma.issue_v(v_rsrc, t * kKvTile, ring.vbuf(t), wave);
         copy_ks(t);
       }
     };
@@ -619,10 +632,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
     auto kbuf = [&](int t) { return smem + (t & 1) * Lds<D>::KBYTES; };
     const LaneOffsets16<D> lo16(lane);
     const DmaOffsets16<D> dma16(wave, lane, a.npad);
-    const uint8_t* vh = (const uint8_t*)(a.v16 + bh * D * a.npad);
+    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(a.v16 + bh * D * a.npad, (int64_t)D * a.npad * 2);
     auto copy_k = [&](int t) {
       if (t < ntiles) {
-        dma.issue_k(kh + (int64_t)t * kKvTile * D, kbuf(t), wave);
+        dma.issue_k(k_rsrc, t * kKvTile * D, kbuf(t), wave);
         copy_ks(t);
       }
     };
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
     init_state();
     auto step = [&](int t, bool masked) {
       tile_barrier<0>();
-      dma16.issue_v(vh + (int64_t)t * kKvTile * 2, vbuf, wave);
+      dma16.issue_v(v_rsrc, t * kKvTile * 2, vbuf, wave);
       copy_k(t + 1);
       qk_tile<D>(kbuf(t), qfr, lo, S);
       softmax_step(t, masked);
@@ -685,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
   const int r = lane & 15, g = lane >> 4;
   const int qrow0 = qb * kBlockM + wave * (G * 16);
   const DmaOffsets<D> dma(wave, lane, npad);
-  dma.issue_k(k_i8 + bh * npad * D + (int64_t)kvt * kKvTile * D, klds, wave);
+  dma.issue_k(make_rsrc(k_i8 + bh * npad * D, npad * D), kvt * kKvTile * D, klds, wave);
   v4i qfr[G][D / 64];
   load_q<D>(q_i8 + bh * npad * D, qrow0, lane, qfr);
   __syncthreads();
