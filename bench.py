@@ -317,7 +317,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(r["attn_tops"] / PEAK_TOPS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "kernel": "k_attn<%d>" % w.d,
+                     "kernel": "k_attn<%d, 0, false>" % w.d,
                      "algorithmic_bytes": 5 * w.B * w.H * w.N * w.d},
         "sweep": sweep,
         "quality_mode": quality,
