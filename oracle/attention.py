@@ -41,6 +41,12 @@ key scale is applied first, y_ij = fp32(S_ij * k_scale_j); the row maximum is ov
 fp32(y_ij * qf_i), and p_ij = exp2(fp32(y_ij * qf_i + nb)) with one rounding (a fused
 multiply-add).  qf_i and nb are as above.
 
+Block-residual K (``quantize(..., k_block_mean=True)``): the key of token j is
+mu_b + K''_j with mu_b the bf16 mean of its 64-token block.  The logit adds the query's
+product with that mean: D_ib = fp32(sum_c q8_ic * mu_bc) (exact sum, one rounding),
+e_ib = fp32(D_ib * qf_i); s_ij = fp32(s'_ij + e_ib) where s'_ij is the logit above,
+and p_ij = exp2(fma(., ., fp32(e_ib + nb))) with the fma operands of the scale mode.
+
 Quality mode (``bf16_p=True, fp8_p=False, fp8_v=False``): the pages mention that
 quantised attention schemes offer a quality-first setting next to the speed-first one
 (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 4.3) and that
@@ -141,7 +147,8 @@ def _exp2_f32(x):
 def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                        quant=None, int8_qk: bool = True, fp8_p: bool = True,
                        fp8_v: bool = True, smooth_k: bool = True,
-                       bf16_p: bool = False, block: int = QUANT_BLOCK) -> np.ndarray:
+                       bf16_p: bool = False, block: int = QUANT_BLOCK,
+                       k_block_mean: bool = False) -> np.ndarray:
     """Quantised attention.  q, k, v: float32 [B, N, H, d] holding bf16 values.
 
     ``quant``: the dict of :func:`oracle.quantize` if already computed.  ``rows``:
@@ -161,8 +168,9 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     B, N, H, d = q.shape
     sm = default_sm_scale(d) if sm_scale is None else float(sm_scale)
     if quant is None:
-        quant = quantize(q, k, v, smooth_k=smooth_k, block=block)
+        quant = quantize(q, k, v, smooth_k=smooth_k, block=block, k_block_mean=k_block_mean)
     qb = int(quant.get("block", QUANT_BLOCK))
+    kbm = quant.get("k_bmean")                       # [B, H, nblk, d] or None
     r = _rows(N, rows)
     L = F32(sm * LOG2E)
     out = np.empty((B, len(r), H, d), dtype=np.float64)
@@ -187,6 +195,14 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                     S = qk_int32(quant["q_i8"][b, h][rr], kq)                 # [R, N]
                     qs = quant["q_scale"][b, h][rr // qb]
                     qf = (qs * L).astype(F32)                                 # [R]
+                    if kbm is not None:
+                        # q8 . mean of each key block, exact then rounded to fp32; times qf
+                        Dq = (quant["q_i8"][b, h][rr].astype(np.float64) @
+                              kbm[b, h].astype(np.float64).T).astype(F32)      # [R, nblk]
+                        E = (Dq.astype(np.float64) * qf[:, None]).astype(F32)
+                        ek = E[:, np.arange(N) // QUANT_BLOCK]                # [R, N]
+                    else:
+                        ek = None
                 else:
                     S = (q[b, rr, h, :].astype(np.float64) @ kf.T) * (sm * LOG2E)
                 m = np.full(R, -np.inf, dtype=F32)
@@ -204,13 +220,18 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                         s = (y.astype(np.float64) * qf[:, None]).astype(F32)
                     else:
                         s = S[:, t0:t1].astype(F32)
+                    if int8_qk and ek is not None:
+                        e = ek[:, t0:t1]
+                        s = (s.astype(np.float64) + e).astype(F32)            # + block-mean term
                     m_new = np.maximum(m, s.max(axis=1))
                     nb = (LOG2_448_F32 - m_new).astype(F32)
+                    nbe = np.broadcast_to(nb[:, None], (len(rr), t1 - t0)).astype(F32)
+                    if int8_qk and ek is not None:
+                        nbe = (e.astype(np.float64) + nbe).astype(F32)
                     if int8_qk and qb > 1:
-                        arg = _fma_f32(x, c, np.broadcast_to(nb[:, None], x.shape))
+                        arg = _fma_f32(x, c, nbe)
                     elif int8_qk:
-                        arg = _fma_f32(y, np.broadcast_to(qf[:, None], y.shape),
-                                       np.broadcast_to(nb[:, None], y.shape))
+                        arg = _fma_f32(y, np.broadcast_to(qf[:, None], y.shape), nbe)
                     else:
                         arg = (s.astype(np.float64) + nb[:, None]).astype(F32)
                     p = _exp2_f32(arg)                                        # [R, t]

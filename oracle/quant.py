@@ -21,6 +21,10 @@ Readings of what the pages leave open (each also listed in the design notes):
   -127, 127) with rint rounding half to even.  The range is symmetric (-128 is never
   produced).  amax = 0 gives scale 0 and all-zero codes.  Scales do not contain the
   softmax scale.
+* Block-residual K (the Sol-Attn variant of the sd114.wiki page, "核心亮点" item 1:
+  only the residual inside each K block is quantised, the mean term stays bf16): the
+  mean of each 64-token block, computed like the token mean, replaces the token mean
+  in the subtraction.
 * FP8 V: one scale per (batch, head, channel) over the valid tokens:
   scale = fp32(vamax / 448); code = e4m3(fp32(v * fp32(448 / vamax))); vamax = 0 gives
   scale 0 and zero codes.
@@ -37,7 +41,7 @@ from .fp8 import e4m3_encode, E4M3_MAX
 
 QUANT_BLOCK = 64
 
-__all__ = ["QUANT_BLOCK", "bf16_round", "k_token_mean", "quantize_int8_blocks",
+__all__ = ["QUANT_BLOCK", "bf16_round", "k_token_mean", "k_block_means", "quantize_int8_blocks",
            "quantize_v_fp8", "quantize"]
 
 F32 = np.float32
@@ -60,6 +64,21 @@ def k_token_mean(k) -> np.ndarray:
     s = k.astype(np.float64).sum(axis=1)               # [B, H, d], fp64
     mean = (s / n).astype(F32)                         # fp64 divide, one fp32 rounding
     return bf16_round(mean)
+
+
+def k_block_means(k, block: int = QUANT_BLOCK) -> np.ndarray:
+    """Per-(b, h, block of `block` tokens, channel) mean of K over the block's valid
+    tokens -> bf16 values as float32 [B, H, nblk, d] (fp64 sum, fp64 divide, fp32 then
+    bf16 rounding, as for the token mean)."""
+    k = np.asarray(k, dtype=F32)
+    B, N, H, d = k.shape
+    nblk = -(-N // block)
+    out = np.zeros((B, H, nblk, d), dtype=F32)
+    for j in range(nblk):
+        r0, r1 = j * block, min(N, (j + 1) * block)
+        s = k[:, r0:r1].astype(np.float64).sum(axis=1)           # [B, H, d]
+        out[:, :, j] = bf16_round((s / (r1 - r0)).astype(F32))
+    return out
 
 
 def quantize_int8_blocks(x, block: int = QUANT_BLOCK):
@@ -107,16 +126,26 @@ def quantize_v_fp8(v):
     return codes, scales
 
 
-def quantize(q, k, v, smooth_k: bool = True, block: int = QUANT_BLOCK) -> dict:
+def quantize(q, k, v, smooth_k: bool = True, block: int = QUANT_BLOCK,
+             k_block_mean: bool = False) -> dict:
     """All quantised operands of one attention call.  q, k, v: float32 [B, N, H, d]
     holding bf16 values.  ``smooth_k=False`` skips the K mean subtraction (used only to
     measure what smoothing buys).  ``block``: tokens per Q/K scale (64, or 1 for one
-    scale per token); it is returned with the operands."""
+    scale per token); it is returned with the operands.  ``k_block_mean``: K keeps a
+    bf16 mean per 64-token block (returned as k_bmean [B, H, nblk, d]) and only the
+    residual is quantised; k_mean is still the token mean."""
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     qh = q.transpose(0, 2, 1, 3)
     kh = k.transpose(0, 2, 1, 3)
-    if smooth_k:
+    N = k.shape[1]
+    kbm = None
+    if k_block_mean:
+        mu = k_token_mean(k)
+        kbm = k_block_means(k)                                   # [B, H, nblk, d]
+        rep = np.repeat(kbm, QUANT_BLOCK, axis=2)[:, :, :N]      # mean of each token's block
+        kr = (kh - rep).astype(F32)                              # fp32 subtraction
+    elif smooth_k:
         mu = k_token_mean(k)                                     # [B, H, d]
         kr = (kh - mu[:, :, None, :]).astype(F32)                # fp32 subtraction
     else:
@@ -125,5 +154,8 @@ def quantize(q, k, v, smooth_k: bool = True, block: int = QUANT_BLOCK) -> dict:
     q_i8, q_scale = quantize_int8_blocks(qh, block)
     k_i8, k_scale = quantize_int8_blocks(kr, block)
     v_f8, v_scale = quantize_v_fp8(v)
-    return dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=mu,
-                v_f8=v_f8, v_scale=v_scale, block=block)
+    out = dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=mu,
+               v_f8=v_f8, v_scale=v_scale, block=block)
+    if kbm is not None:
+        out["k_bmean"] = kbm
+    return out

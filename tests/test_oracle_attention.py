@@ -264,3 +264,34 @@ def test_per_token_uniform_case_and_scales():
     p = np.exp(s - s.max(axis=1, keepdims=True))
     want = (p / p.sum(axis=1, keepdims=True)) @ v2[0, :, 0, :].astype(np.float64)
     assert np.abs(got[0, :, 0, :] - want).max() < 2e-5
+
+
+# ---- block-residual K ----
+
+def test_block_mean_closed_form_block_constant_keys():
+    # K constant inside every 64-token block (different across blocks): the block
+    # means reproduce K exactly, the residual codes are 0, and with unrounded P and V
+    # the pipeline is the exact softmax of (dequantised Q) . K^T
+    q, k, v = _qkv(1, 150, 2, 32, seed=31, kbias=2.0)
+    for j in range(0, 150, 64):
+        k[:, j:j + 64] = k[:, j:j + 1]
+    quant = oracle.quantize(q, k, v, k_block_mean=True)
+    assert not quant["k_i8"].any()
+    got = attention_pipeline(q, k, v, kv_tile=64, quant=quant, fp8_p=False, fp8_v=False)
+    for h in range(2):
+        qd = quant["q_i8"][0, h].astype(np.float64) * np.repeat(quant["q_scale"][0, h], 64)[:150, None]
+        s = qd @ k[0, :, h, :].astype(np.float64).T / np.sqrt(32)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        want = (p / p.sum(axis=1, keepdims=True)) @ v[0, :, h, :].astype(np.float64)
+        assert np.abs(got[0, :, h, :] - want).max() < 1e-5
+
+
+def test_block_mean_error_budget_matches_token_mean_on_synthetic_keys():
+    # the synthetic keys have no token-local structure, so block means neither help
+    # nor hurt noticeably
+    w = workloads.get("tiny")
+    q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+    ex = attention_exact(q, k, v)
+    r_tok = oracle.rel_l2(attention_pipeline(q, k, v, kv_tile=128), ex)
+    r_blk = oracle.rel_l2(attention_pipeline(q, k, v, kv_tile=128, k_block_mean=True), ex)
+    assert abs(r_blk - r_tok) < 0.003

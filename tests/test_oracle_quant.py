@@ -55,6 +55,19 @@ def test_k_mean_equals_exact_rational_mean_rounded():
                 assert mu[b, h, c] == want
 
 
+def test_k_block_means_equal_exact_rational_means_rounded():
+    from oracle.quant import k_block_means
+    k = _bf16_values((1, 150, 2, 4), seed=12, scale=1.0, shift=1.5)
+    mu = k_block_means(k)
+    assert mu.shape == (1, 2, 3, 4)
+    for h in range(2):
+        for j, (r0, r1) in enumerate([(0, 64), (64, 128), (128, 150)]):
+            for c in range(4):
+                exact = sum(Fraction(float(x)) for x in k[0, r0:r1, h, c]) / (r1 - r0)
+                want = bf16_round(np.array([_f32_rne_of_fraction(exact)], F32))[0]
+                assert mu[0, h, j, c] == want
+
+
 def test_k_mean_is_bitwise_permutation_invariant():
     k = _bf16_values((1, 301, 2, 16), seed=3, scale=1.0, shift=-4.0)
     perm = np.random.default_rng(0).permutation(301)
