@@ -50,9 +50,14 @@ def quant_bytes(w) -> float:
     return 9.0 * E
 
 
-def measure_quality(w, steps, warmup, per_token=False):
-    """Whole-step time of the quality mode (INT8 Q.K^T, bf16 P.V; optionally per-token
-    Q/K scales) on workload w."""
+# the optional modes of sage_attn_fwd_ex that the bench times (whole step)
+MODES = {"bf16_pv": dict(pv="bf16"),
+         "bf16_pv_per_token": dict(pv="bf16", per_token=True),
+         "fp8_pv_block_mean_k": dict(pv="fp8", k_block_mean=True)}
+
+
+def measure_mode(w, steps, warmup, **opts):
+    """Whole-step time of sage_attn_fwd_ex with options ``opts`` on workload w."""
     import torch
     import workloads
     import quantized_attention_diffusion_amd as sage
@@ -60,16 +65,16 @@ def measure_quality(w, steps, warmup, per_token=False):
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
     out = torch.empty_like(q)
-    mode = sage.mode_bits("bf16", per_token)
+    mode = sage.mode_bits(**opts)
     ws = torch.empty(sage.sage_workspace_bytes_ex(w.B, w.H, w.N, w.d, mode), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16", per_token=per_token)
+        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, **opts)
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
-        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16", per_token=per_token)
+        sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, **opts)
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
@@ -286,10 +291,9 @@ def main():
                            "quant_gbs": round(rs["quant_gbs"], 1)}
         for name in SWEEP + [w.name]:
             wq = workloads.get(name)
-            print(f"[bench] quality modes {name} N={wq.N}", file=sys.stderr, flush=True)
+            print(f"[bench] optional modes {name} N={wq.N}", file=sys.stderr, flush=True)
             st, wu = (args.steps, args.warmup) if name == w.name else (SWEEP_STEPS, 2)
-            quality[name] = {"bf16_pv": measure_quality(wq, st, wu),
-                             "bf16_pv_per_token": measure_quality(wq, st, wu, per_token=True)}
+            quality[name] = {mname: measure_mode(wq, st, wu, **opts) for mname, opts in MODES.items()}
     print(f"[bench] {w.name} B={w.B} H={w.H} N={w.N} d={w.d}: {args.warmup} warmup + {args.steps} steps",
           file=sys.stderr, flush=True)
     r = measure(w, args.steps, args.warmup)
@@ -320,7 +324,7 @@ def main():
                      "kernel": "k_attn<%d, 0, false>" % w.d,
                      "algorithmic_bytes": 5 * w.B * w.H * w.N * w.d},
         "sweep": sweep,
-        "quality_mode": quality,
+        "modes": quality,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

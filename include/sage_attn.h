@@ -70,7 +70,8 @@ enum {
 enum {
     SAGE_PV_FP8 = 0,           /* P and V in FP8 e4m3 (speed; the default) */
     SAGE_PV_BF16 = 1,          /* P rounded to bf16, V unquantised bf16 (quality) */
-    SAGE_QK_PER_TOKEN = 2      /* one INT8 scale per Q and K token instead of per 64 */
+    SAGE_QK_PER_TOKEN = 2,     /* one INT8 scale per Q and K token instead of per 64 */
+    SAGE_K_BLOCK_MEAN = 4      /* block-residual K: bf16 mean per 64-key block (FP8 P.V only) */
 };
 
 typedef struct sage_info {
@@ -123,7 +124,8 @@ int sage_quant_qk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /* sage_quant_qk with mode bits (see sage_attn_fwd_ex): SAGE_QK_PER_TOKEN gives per-token
  * q_scale/k_scale [B][H][Npad]; SAGE_PV_BF16 writes bf16 V [B][H][d][Npad] into v_f8
- * (sized 2 bytes per element) and leaves v_scale unwritten. */
+ * (sized 2 bytes per element) and leaves v_scale unwritten; SAGE_K_BLOCK_MEAN writes
+ * the block means [B][H][Npad/64][d] into k_mean (zero for all-padding blocks). */
 int sage_quant_qk_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const sage_strides* sq, const sage_strides* sk, const sage_strides* sv,
                      int B, int H, int N, int d, int mode,
@@ -177,6 +179,14 @@ int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
  *     token's d channels; same rounding), q_scale/k_scale become [B][H][Npad].  The
  *     logit arithmetic applies the key scale first: y = fp32(S * k_scale_j), the row
  *     maximum is over fp32(y * qf), p = 448 * 2^(s - m) = exp2(fma(y, qf, log2(448) - m)).
+ *   SAGE_K_BLOCK_MEAN: block-residual K (sd114.wiki ComfyUI-sol-attn page, "核心亮点"
+ *     item 1: only the residual inside each K block is quantised, the mean term stays
+ *     bf16).  k_mean becomes [B][H][Npad/64][d]: the bf16 mean of each 64-token block's
+ *     valid tokens (fp64 sum, fp32 then bf16 rounding); K' = fp32(K) - fp32(block mean)
+ *     is coded as usual.  The logits gain e = fp32(qf * D), D = q8 . block mean (bf16
+ *     matrix cores, fp32 accumulation): s = fp32(fp32(S * c) + e) for the maximum (with
+ *     per-token scales fp32(fp32(y * qf) + e)) and p = exp2(fma(., ., fp32(e + nb))).
+ *     Only with SAGE_PV_FP8 (with SAGE_PV_BF16: SAGE_EUNSUPPORTED).
  * mode 0 is identical to sage_attn_fwd.  Unknown bits return SAGE_EINVAL.  The
  * workspace size comes from sage_workspace_bytes_ex with the same mode.
  */

@@ -12,7 +12,8 @@ __all__ = ["SageError", "lib_path", "load", "sage_last_error", "sage_kernel_info
            "sage_padded_tokens", "sage_workspace_bytes", "sage_workspace_bytes_ex",
            "sage_quant_scratch_bytes", "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd",
            "sage_attn_fwd_ex", "sage_quant_qk_ex", "sage_debug_qk_i32", "sage_debug_e4m3",
-           "EXPORTS", "STATUS", "SAGE_PV_FP8", "SAGE_PV_BF16", "SAGE_QK_PER_TOKEN", "mode_bits"]
+           "EXPORTS", "STATUS", "SAGE_PV_FP8", "SAGE_PV_BF16", "SAGE_QK_PER_TOKEN",
+           "SAGE_K_BLOCK_MEAN", "mode_bits"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(HERE, "libsage_attn.so")
@@ -25,15 +26,16 @@ EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
            "sage_quant_qk", "sage_quant_qk_ex", "sage_attn_fwd_prequant", "sage_attn_fwd",
            "sage_attn_fwd_ex", "sage_debug_qk_i32", "sage_debug_e4m3"]
 
-SAGE_PV_FP8, SAGE_PV_BF16, SAGE_QK_PER_TOKEN = 0, 1, 2
+SAGE_PV_FP8, SAGE_PV_BF16, SAGE_QK_PER_TOKEN, SAGE_K_BLOCK_MEAN = 0, 1, 2, 4
 
 
-def mode_bits(pv: str = "fp8", per_token: bool = False) -> int:
-    """The C mode bits for P.V precision ``pv`` ('fp8' or 'bf16') and per-token Q/K
-    scales."""
+def mode_bits(pv: str = "fp8", per_token: bool = False, k_block_mean: bool = False) -> int:
+    """The C mode bits for P.V precision ``pv`` ('fp8' or 'bf16'), per-token Q/K scales
+    and block-residual K."""
     if pv not in ("fp8", "bf16"):
         raise ValueError(f"pv must be 'fp8' or 'bf16', got {pv!r}")
-    return (SAGE_PV_BF16 if pv == "bf16" else 0) | (SAGE_QK_PER_TOKEN if per_token else 0)
+    return ((SAGE_PV_BF16 if pv == "bf16" else 0) | (SAGE_QK_PER_TOKEN if per_token else 0) |
+            (SAGE_K_BLOCK_MEAN if k_block_mean else 0))
 
 
 class SageError(RuntimeError):
@@ -175,7 +177,8 @@ def _alloc_quant(B, H, N, d, dev, mode=0):
         q_scale=torch.empty((B, H, nsc), dtype=torch.float32, device=dev),
         k_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
         k_scale=torch.empty((B, H, nsc), dtype=torch.float32, device=dev),
-        k_mean=torch.empty((B, H, d), dtype=torch.bfloat16, device=dev),
+        k_mean=torch.empty((B, H, npad // 64, d) if mode & SAGE_K_BLOCK_MEAN else (B, H, d),
+                           dtype=torch.bfloat16, device=dev),
         v_f8=torch.empty((B, H, d, npad), dtype=vdt, device=dev),
         v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev),
     )
@@ -253,12 +256,12 @@ def sage_attn_fwd(q, k, v, out: torch.Tensor | None = None, sm_scale: float | No
 
 def sage_attn_fwd_ex(q, k, v, out: torch.Tensor | None = None, sm_scale: float | None = None,
                      layout: str = "bnhd", workspace: torch.Tensor | None = None,
-                     pv: str = "fp8", per_token: bool = False,
+                     pv: str = "fp8", per_token: bool = False, k_block_mean: bool = False,
                      _entry: str = "sage_attn_fwd_ex") -> torch.Tensor:
-    """sage_attn_fwd with quality options: ``pv`` = 'fp8' (speed, the default path) or
-    'bf16' (P rounded to bf16, V unquantised); ``per_token``: one INT8 scale per Q and
-    K token."""
-    mode = mode_bits(pv, per_token)
+    """sage_attn_fwd with options: ``pv`` = 'fp8' (speed, the default path) or 'bf16'
+    (P rounded to bf16, V unquantised); ``per_token``: one INT8 scale per Q and K token;
+    ``k_block_mean``: block-residual K (FP8 P.V only)."""
+    mode = mode_bits(pv, per_token, k_block_mean)
     for n, t in (("q", q), ("k", k), ("v", v)):
         _bf16_cuda(n, t)
     (B, H, N, d), sq = _dims(q, layout)

@@ -107,7 +107,7 @@ QuantLayout layout(int B, int H, int N, int d, int mode = 0) {
   L.v_f8 = bh * L.npad * d * ((mode & SAGE_PV_BF16) ? 2 : 1);
   L.q_scale = L.k_scale =
       bh * ((mode & SAGE_QK_PER_TOKEN) ? L.npad : L.npad / sage::kQuantBlock) * sizeof(float);
-  L.k_mean = bh * d * sizeof(uint16_t);
+  L.k_mean = bh * d * sizeof(uint16_t) * ((mode & SAGE_K_BLOCK_MEAN) ? L.npad / sage::kQuantBlock : 1);
   L.v_scale = bh * d * sizeof(float);
   const size_t chunks = sage::stats_chunks(N);
   L.ksum = bh * chunks * d * sizeof(double);
@@ -169,8 +169,11 @@ SAGE_EXPORT int sage_quant_scratch_bytes(int B, int H, int N, int d, size_t* byt
 }
 
 static int check_mode(int mode) {
-  if (mode & ~(SAGE_PV_BF16 | SAGE_QK_PER_TOKEN))
-    return fail(SAGE_EINVAL, "mode %#x has bits other than SAGE_PV_BF16 | SAGE_QK_PER_TOKEN", mode);
+  if (mode & ~(SAGE_PV_BF16 | SAGE_QK_PER_TOKEN | SAGE_K_BLOCK_MEAN))
+    return fail(SAGE_EINVAL, "mode %#x has bits other than SAGE_PV_BF16 | SAGE_QK_PER_TOKEN | SAGE_K_BLOCK_MEAN",
+                mode);
+  if ((mode & SAGE_PV_BF16) && (mode & SAGE_K_BLOCK_MEAN))
+    return fail(SAGE_EUNSUPPORTED, "SAGE_K_BLOCK_MEAN is implemented with FP8 P.V only");
   return SAGE_OK;
 }
 
@@ -234,6 +237,7 @@ SAGE_EXPORT int sage_quant_qk_ex(const uint16_t* q, const uint16_t* k, const uin
   a.pv = (mode & SAGE_PV_BF16) ? sage::kPvBf16 : sage::kPvFp8;
   a.v16 = (mode & SAGE_PV_BF16) ? (uint16_t*)v_f8 : nullptr;
   a.tok = (mode & SAGE_QK_PER_TOKEN) ? 1 : 0;
+  a.kbm = (mode & SAGE_K_BLOCK_MEAN) ? 1 : 0;
   char* p = (char*)scratch;
   carve_scratch(p, L, a);
   return launch_status(sage::launch_quant(a, (hipStream_t)stream), "quantisation");
@@ -275,6 +279,7 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
   sage::AttnArgs a;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale;
   a.v_f8 = v_f8; a.v_scale = v_scale; a.v16 = nullptr; a.pv = sage::kPvFp8; a.tok = 0;
+  a.k_bmean = nullptr;
   a.out = out; a.so = to_internal(*so);
   a.B = B; a.H = H; a.N = N; a.d = d; a.npad = L.npad;
   a.log2e_scale = log2e_scale(sm_scale);
@@ -326,6 +331,7 @@ SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uin
   qa.pv = (mode & SAGE_PV_BF16) ? sage::kPvBf16 : sage::kPvFp8;
   qa.v16 = (mode & SAGE_PV_BF16) ? (uint16_t*)qa.v_f8 : nullptr;
   qa.tok = (mode & SAGE_QK_PER_TOKEN) ? 1 : 0;
+  qa.kbm = (mode & SAGE_K_BLOCK_MEAN) ? 1 : 0;
   carve_scratch(p, L, qa);
   hipStream_t s = (hipStream_t)stream;
   if (int rc = launch_status(sage::launch_quant(qa, s), "quantisation")) return rc;
@@ -333,6 +339,7 @@ SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uin
   sage::AttnArgs a;
   a.q_i8 = qa.q_i8; a.q_scale = qa.q_scale; a.k_i8 = qa.k_i8; a.k_scale = qa.k_scale;
   a.v_f8 = qa.v_f8; a.v_scale = qa.v_scale; a.v16 = qa.v16; a.pv = qa.pv; a.tok = qa.tok;
+  a.k_bmean = qa.kbm ? qa.k_mean : nullptr;
   a.out = out; a.so = to_internal(strides[3]);
   a.B = B; a.H = H; a.N = N; a.d = d; a.npad = L.npad;
   a.log2e_scale = log2e_scale(sm_scale);

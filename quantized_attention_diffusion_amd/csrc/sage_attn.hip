@@ -285,9 +285,9 @@ __device__ __forceinline__ void pv_tile16(const uint8_t* vbuf, const PTile<kPvBf
 // keys at tile index >= nvalid are removed by giving them the logit -inf; a lane whose
 // c is 0 then uses x = 0 and c = 1 for its valid keys, which yields the same s = 0 and
 // p = 448 * 2^-m without forming -inf * 0.
-template <bool MASKED, int PV>
+template <bool MASKED, int PV, bool BM = false>
 __device__ __forceinline__ float softmax_group(v4i (&S)[8], float c, int nvalid, float log2_pscale,
-                                               float& m, float& lpart, PTile<PV>& P, int g) {
+                                               float& m, float& lpart, PTile<PV>& P, int g, float e = 0.0f) {
   float xf[8][4];
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt)
@@ -309,10 +309,10 @@ __device__ __forceinline__ float softmax_group(v4i (&S)[8], float c, int nvalid,
 #pragma unroll
     for (int i = 0; i < 4; ++i) xm = fmaxf(xm, xf[kt][i]);
   // c >= 0 and rounding is monotone, so this is the max of fp32(x * c) over the keys
-  float sl = (xm == -INFINITY) ? -INFINITY : xm * c;
+  float sl = (xm == -INFINITY) ? -INFINITY : (BM ? xm * c + e : xm * c);
   sl = max_over_lane_groups(sl);
   const float m_new = fmaxf(m, sl);
-  const float nb = log2_pscale - m_new;
+  const float nb = BM ? e + (log2_pscale - m_new) : log2_pscale - m_new;
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);
   float lsum = 0.0f;
 #pragma unroll
@@ -343,10 +343,10 @@ __device__ __forceinline__ void rescale(v4f (&acc)[D / 16], float alpha) {
 // row max (exact, no NaN handling), fp32 conversion (exact: |S| < 2^24), exp2 of the
 // fused multiply-add, rounding into P, independent partial row sums.  Same
 // arithmetic as softmax_group<false>; the two groups' work is interleaved for ILP.
-template <int PV>
+template <int PV, bool BM = false>
 __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G], float log2_pscale,
                                              float (&m)[G], float (&lpart)[G], PTile<PV> (&P)[G],
-                                             float (&alpha)[G]) {
+                                             float (&alpha)[G], const float (&e)[G]) {
   int xmi[G];
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
@@ -362,10 +362,11 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
   float nb[G], m_new[G];
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
-    // c >= 0 and rounding is monotone: this is the max of fp32(x * c) over the keys
-    const float sl = max_over_lane_groups((float)xmi[gq] * c[gq]);
+    // c >= 0 and rounding is monotone: this is the max of fp32(x * c) (+ e) over the keys
+    const float xs = (float)xmi[gq] * c[gq];
+    const float sl = max_over_lane_groups(BM ? xs + e[gq] : xs);
     m_new[gq] = fmaxf(m[gq], sl);
-    nb[gq] = log2_pscale - m_new[gq];
+    nb[gq] = BM ? e[gq] + (log2_pscale - m_new[gq]) : log2_pscale - m_new[gq];
     alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
   }
   float ls[G][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -388,15 +389,19 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
   }
 }
 
+// With BM (block-residual K) the logits gain e = fp32(qf * q8.mean_block), constant over
+// the lane's 32 keys: the maximum is taken over fp32(. + e) and e is added to nb.
+//
 // Online-softmax update of both query groups with per-token scales: ks[kt][i] is the
 // scale of tile key 32g + 4kt + i and qf the query factor fp32(q_scale * sm_scale *
 // log2 e).  y = fp32(S * ks) per key; the row maximum is the max of fp32(y * qf) (qf >= 0
 // and rounding is monotone, so it is fp32(max y * qf)); p = exp2(fma(y, qf, nb)).  When
 // MASKED, keys at tile index >= nvalid get p = 0 and take no part in the maximum.
-template <int PV, bool MASKED>
+template <int PV, bool MASKED, bool BM = false>
 __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const v4f (&ks)[8], const float (&qf)[G],
                                                  int nvalid, int g, float log2_pscale, float (&m)[G],
-                                                 float (&lpart)[G], PTile<PV> (&P)[G], float (&alpha)[G]) {
+                                                 float (&lpart)[G], PTile<PV> (&P)[G], float (&alpha)[G],
+                                                 const float (&e)[G]) {
   float y[G][8][4];
   float ym[G];
 #pragma unroll
@@ -420,9 +425,10 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const v4f (&ks)
   float nb[G], m_new[G];
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
-    const float sl = max_over_lane_groups(ym[gq] == -INFINITY ? -INFINITY : ym[gq] * qf[gq]);
+    const float ys = ym[gq] * qf[gq];
+    const float sl = max_over_lane_groups(ym[gq] == -INFINITY ? -INFINITY : (BM ? ys + e[gq] : ys));
     m_new[gq] = fmaxf(m[gq], sl);
-    nb[gq] = log2_pscale - m_new[gq];
+    nb[gq] = BM ? e[gq] + (log2_pscale - m_new[gq]) : log2_pscale - m_new[gq];
     alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
   }
   float ls[G][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -462,6 +468,56 @@ __device__ __forceinline__ void load_kscale(const uint8_t* lds, int g, v4f (&ks)
   for (int kt = 0; kt < 8; ++kt) ks[kt] = *(const v4f*)(lds + 128 * g + 16 * kt);
 }
 
+// Block-residual K: the bf16 means of the tile's two 64-key blocks (2 x D values) are
+// staged in LDS next to the K tile, D bytes per wave (D/16 lanes of one DMA instruction).
+template <int D>
+__device__ __forceinline__ void issue_kbmean(__amdgpu_buffer_rsrc_t r, int tile_off, uint8_t* lds, int wave, int lane) {
+  if (lane < D / 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds + D * wave), 16, D * wave + 16 * lane,
+                                             tile_off, 0, 0);
+}
+
+// The query's INT8 codes as bf16 (exact), in the operand order of the mean products:
+// qb[gq][kk][h] = channels 64kk + 16g + 8h .. +7 of query r, from qfr[gq][kk].
+template <int D>
+__device__ __forceinline__ void q_codes_bf16(const v4i (&qfr)[G][D / 64], v4i (&qb)[G][D / 64][2]) {
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq)
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int word = qfr[gq][kk][2 * h + (w >> 1)];
+          const int sh = 16 * (w & 1);
+          const float lo = (float)(int8_t)(word >> sh), hi = (float)(int8_t)(word >> (sh + 8));
+          qb[gq][kk][h][w] = pk_bf16(lo, hi);
+        }
+}
+
+// e[gq] = fp32(qf * D) with D = q8 . mean of this lane's key block (bf16 matrix cores,
+// fp32 accumulation): rows of the row operand are the two block means (rows 0-7 block
+// 0, 8-15 block 1), columns the queries, so lane (r, g) finds D for query r and block
+// g/2 in register 0.
+template <int D>
+__device__ __forceinline__ void block_mean_terms(const uint8_t* kbm_lds, const v4i (&qb)[G][D / 64][2],
+                                                 const float (&qf)[G], int r, int g, float (&e)[G]) {
+  v4f acc[G] = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i mf = *(const v4i*)(kbm_lds + (r >> 3) * 2 * D + 128 * kk + 32 * g + 16 * h);
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq)
+        acc[gq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mf),
+                                                          __builtin_bit_cast(v8bf, qb[gq][kk][h]), acc[gq], 0, 0, 0);
+    }
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) e[gq] = acc[gq][0] * qf[gq];
+}
+
 // Maps the linear workgroup id to (head, query block) so that the workgroups one XCD
 // receives (ids x, x+8, x+16, ... go to XCD x) are consecutive query blocks of the same
 // heads and share that head's K/V tiles in the XCD's L2.
@@ -499,21 +555,27 @@ struct Ring {
   __device__ __forceinline__ uint8_t* vbuf(int t) const { return smem + (t % kStages) * STAGE + Lds<D>::KBYTES; }
 };
 
-template <int D, int PV, bool TOK>
+template <int D, int PV, bool TOK, bool KBM>
 struct AttnSmem {
   static constexpr int MAIN = PV == kPvFp8 ? kStages * Ring<D>::STAGE
                                            : 2 * Lds<D>::KBYTES + Lds<D>::V16BYTES;
   static constexpr int KSCALE = TOK ? 2 * 512 : 0;   // per-token key scales, 2 buffers
-  static constexpr int BYTES = MAIN + KSCALE;
+  static constexpr int KBMEAN = KBM ? 2 * 4 * D : 0; // two block means per tile, 2 buffers
+  static constexpr int BYTES = MAIN + KSCALE + KBMEAN;
 };
 
 // TOK: per-token Q/K scales (q_scale, k_scale [B][H][Npad]); the key scales of each
-// tile are staged in LDS with the K tile.
-template <int D, int PV, bool TOK>
+// tile are staged in LDS with the K tile.  KBM: block-residual K; the block means of
+// each tile are staged likewise and their products with the query codes are added to
+// the logits.
+template <int D, int PV, bool TOK, bool KBM>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[AttnSmem<D, PV, TOK>::BYTES];
-  uint8_t* const ksmem = smem + AttnSmem<D, PV, TOK>::MAIN;
+  using Smem = AttnSmem<D, PV, TOK, KBM>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Smem::BYTES];
+  uint8_t* const ksmem = smem + Smem::MAIN;
   auto ksbuf = [&](int t) { return ksmem + (t & 1) * 512; };
+  uint8_t* const kbmem = smem + Smem::MAIN + Smem::KSCALE;
+  auto kbmbuf = [&](int t) { return kbmem + (t & 1) * 4 * D; };
 
   // workgroup-uniform indices kept in scalar registers (readfirstlane), so that the
   // per-tile k_scale reads are scalar loads and never wait on the vector-memory counter
@@ -555,26 +617,37 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
     for (int gq = 0; gq < G; ++gq) c[gq] = qf[gq] * ks;
   };
   const __amdgpu_buffer_rsrc_t ks_rsrc = make_rsrc(a.k_scale + bh * a.npad, TOK ? a.npad * 4 : 0);
+  const __amdgpu_buffer_rsrc_t kbm_rsrc = make_rsrc(KBM ? a.k_bmean + bh * nblk * D : a.k_bmean,
+                                                    KBM ? nblk * D * 2 : 0);
+  // the per-tile side copies that go with the K tile (key scales, block means)
   auto copy_ks = [&](int t) {
     if constexpr (TOK) {
       if (t < ntiles) issue_kscale(ks_rsrc, t * kKvTile * 4, ksbuf(t), wave, lane);
     }
+    if constexpr (KBM) {
+      if (t < ntiles) issue_kbmean<D>(kbm_rsrc, t * 4 * D, kbmbuf(t), wave, lane);
+    }
   };
+  constexpr int SIDE = (TOK ? 1 : 0) + (KBM ? 1 : 0);   // side copies per wave and tile
+  v4i qcb[G][D / 64][2];                               // query codes as bf16 (KBM)
+  float e[G] = {};
   // softmax of tile t, masked to `tail` keys or not
   auto softmax_step = [&](int t, bool masked) {
+    if constexpr (KBM) block_mean_terms<D>(kbmbuf(t), qcb, qf, r, g, e);
     if constexpr (TOK) {
       v4f ks[8];
       load_kscale(ksbuf(t), g, ks);
-      if (!masked) softmax_tile_tok<PV, false>(S, ks, qf, kKvTile, g, a.log2_pscale, m, lpart, P, alpha);
-      else softmax_tile_tok<PV, true>(S, ks, qf, tail, g, a.log2_pscale, m, lpart, P, alpha);
+      if (!masked) softmax_tile_tok<PV, false, KBM>(S, ks, qf, kKvTile, g, a.log2_pscale, m, lpart, P, alpha, e);
+      else softmax_tile_tok<PV, true, KBM>(S, ks, qf, tail, g, a.log2_pscale, m, lpart, P, alpha, e);
     } else {
       scale_products(t);
       if (!masked) {
-        softmax_tile<PV>(S, c, a.log2_pscale, m, lpart, P, alpha);
+        softmax_tile<PV, KBM>(S, c, a.log2_pscale, m, lpart, P, alpha, e);
       } else {
 #pragma unroll
         for (int gq = 0; gq < G; ++gq)
-          alpha[gq] = softmax_group<true, PV>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq], g);
+          alpha[gq] = softmax_group<true, PV, KBM>(S[gq], c[gq], tail, a.log2_pscale, m[gq], lpart[gq], P[gq],
+                                                   g, e[gq]);
       }
     }
   };
@@ -588,6 +661,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) acc[gq][dt] = v4f{0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (KBM) q_codes_bf16<D>(qfr, qcb);
   };
 
   if constexpr (PV == kPvFp8) {
@@ -604,7 +678,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
     for (int t = 0; t < kStages - 1; ++t) copy_tile(t);
     load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
     init_state();
-    constexpr int KEEP = (kStages - 2) * (DmaOffsets<D>::PER_TILE + (TOK ? 1 : 0));
+    constexpr int KEEP = (kStages - 2) * (DmaOffsets<D>::PER_TILE + SIDE);
     for (int t = 0; t < nfull; ++t) {
       // tile t has landed once only the copies of the kStages-2 later tiles may be in flight
       if (t + kStages - 2 < ntiles) tile_barrier<KEEP>();
@@ -651,7 +725,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
       // V(t) must have landed; the copies of tile t+1 (K and key scales) may be in flight
-      if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW + (TOK ? 1 : 0)>();
+      if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW + SIDE>();
       else tile_barrier<0>();
       pv_tile16<D>(vbuf, P, lo16, acc);
     };
@@ -716,12 +790,21 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
   }
 }
 
+template <int D, int PV, bool TOK>
+static void launch_attn_kbm(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if constexpr (PV == kPvFp8) {
+    if (a.k_bmean) {
+      hipLaunchKernelGGL((k_attn<D, PV, TOK, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_attn<D, PV, TOK, false>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
 template <int D, int PV>
 static void launch_attn_tok(const AttnArgs& a, unsigned grid, hipStream_t s) {
-  if (a.tok)
-    hipLaunchKernelGGL((k_attn<D, PV, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn<D, PV, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.tok) launch_attn_kbm<D, PV, true>(a, grid, s);
+  else launch_attn_kbm<D, PV, false>(a, grid, s);
 }
 
 template <int D>
@@ -753,14 +836,18 @@ hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_
 
 // explicit instantiations: the host pass does not always emit launch stubs for kernel
 // templates that are only named inside hipLaunchKernelGGL
-template __global__ void k_attn<64, kPvFp8, false>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, false>(AttnArgs);
-template __global__ void k_attn<64, kPvBf16, false>(AttnArgs);
-template __global__ void k_attn<128, kPvBf16, false>(AttnArgs);
-template __global__ void k_attn<64, kPvFp8, true>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, true>(AttnArgs);
-template __global__ void k_attn<64, kPvBf16, true>(AttnArgs);
-template __global__ void k_attn<128, kPvBf16, true>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false, true>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true, true>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, false, false>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, true, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false, true>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true, true>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, false, false>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, true, false>(AttnArgs);
 template __global__ void k_debug_qk<64>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,
                                         int64_t, int, int, int, int32_t* __restrict__);
 template __global__ void k_debug_qk<128>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,

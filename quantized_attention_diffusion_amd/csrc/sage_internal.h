@@ -55,6 +55,7 @@ struct QuantArgs {
   uint16_t* v16;       // kPvBf16: bf16 V [B][H][d][Npad]
   int pv;              // PvMode
   int tok;             // 1: Q/K scales per token [B][H][Npad], 0: per 64-token block
+  int kbm;             // 1: block-residual K, k_mean holds [B][H][Npad/64][d] block means
   double* ksum_part;   // [B*H][chunks][d]
   float* vmax_part;    // [B*H][chunks][d]
   float* v_inv;        // [B*H][d]
@@ -71,6 +72,7 @@ struct AttnArgs {
   const uint16_t* v16;
   int pv;              // PvMode
   int tok;             // Q/K scales per token
+  const uint16_t* k_bmean;  // block-residual K: bf16 block means [B][H][Npad/64][d], or null
   uint16_t* out;
   Strides so;
   int B, H, N, d;

@@ -88,7 +88,8 @@ __device__ __forceinline__ void load_block(const uint16_t* base, int64_t stride_
 // NEED_V: the speed mode also needs the per-channel max |V| (e4m3 V scales); the
 // quality mode keeps V in bf16 and skips it.
 // TOK: one INT8 scale per token (q_scale [B][H][Npad]) instead of per 64-token block.
-template <int D, bool NEED_V, bool TOK>
+// NEED_KSUM: the token mean of K is needed (not with block-residual K).
+template <int D, bool NEED_V, bool TOK, bool NEED_KSUM>
 __global__ __launch_bounds__(256) void k_quant_q_stats(
     const uint16_t* __restrict__ q, Strides sq, const uint16_t* __restrict__ k, Strides sk,
     const uint16_t* __restrict__ v, Strides sv, int H, int N, int64_t npad, int blocks_per_chunk,
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
     const int row0 = blk * kQuantBlock;
     uint4 qw[RPT], kw[RPT], vw[RPT];
     load_block<RPT, RPI>(qb, sq.n, row0, r, N, qw);
-    load_block<RPT, RPI>(kb, sk.n, row0, r, N, kw);
+    if constexpr (NEED_KSUM) load_block<RPT, RPI>(kb, sk.n, row0, r, N, kw);
     if constexpr (NEED_V) load_block<RPT, RPI>(vb, sv.n, row0, r, N, vw);
     float x[RPT][8];
     uint2 codes[RPT];
@@ -139,10 +140,12 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
       *(uint2*)(q_i8 + (bh * npad + row0 + r + RPI * i) * D + 8 * cg) = codes[i];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      float kx[8];
-      bf16x8_to_f32(kw[i], kx);
+      if constexpr (NEED_KSUM) {
+        float kx[8];
+        bf16x8_to_f32(kw[i], kx);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] += (double)kx[j];
+        for (int j = 0; j < 8; ++j) s[j] += (double)kx[j];
+      }
       if constexpr (NEED_V) {
         float vx[8];
         bf16x8_to_f32(vw[i], vx);
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
 // One workgroup per (b, h): 1024 threads = D channels x (1024 / D) slices of the
 // partial rows, combined through LDS in slice order.
 constexpr int kFinalizeThreads = 1024;
-template <int D, bool NEED_V>
+template <int D, bool NEED_V, bool NEED_K>
 __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
     const double* __restrict__ ksum_part, const float* __restrict__ vmax_part, int chunks, int N,
     uint16_t* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
   float vm = 0.0f;
 #pragma unroll 4
   for (int i = sl; i < chunks; i += SL) {
-    s += ksum_part[(bh * chunks + i) * D + c];
+    if constexpr (NEED_K) s += ksum_part[(bh * chunks + i) * D + c];
     if constexpr (NEED_V) vm = fmaxf(vm, vmax_part[(bh * chunks + i) * D + c]);
   }
   ps[sl][c] = s;
@@ -190,8 +193,10 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
   if (sl == 0) {
 #pragma unroll
     for (int i = 1; i < SL; ++i) { s += ps[i][c]; vm = fmaxf(vm, pv[i][c]); }
-    const float mean = (float)(s / (double)N);        // fp64 divide, one rounding to fp32
-    k_mean[bh * D + c] = (uint16_t)f32_to_bf16_rne(mean);
+    if constexpr (NEED_K) {
+      const float mean = (float)(s / (double)N);      // fp64 divide, one rounding to fp32
+      k_mean[bh * D + c] = (uint16_t)f32_to_bf16_rne(mean);
+    }
     if constexpr (NEED_V) {
       v_scale[bh * D + c] = vm / kPScale;             // IEEE division (0 when vm = 0)
       v_inv[bh * D + c] = vm > 0.0f ? kPScale / vm : 0.0f;
@@ -207,10 +212,14 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_quant_finalize(
 //
 // V16 (quality mode): V keeps its bf16 values and is only transposed: each thread's
 // RPT tokens of a channel (2*RPT bytes) go to LDS as RPT/2 words in rows of 33 words.
-template <int D, bool V16, bool TOK>
+//
+// KBM (block-residual K): the mean subtracted from K is that of the block's own valid
+// tokens (fp64 sums reduced through LDS, then fp32 and bf16 rounding like the token
+// mean), written to k_mean [B][H][Npad/64][d].
+template <int D, bool V16, bool TOK, bool KBM>
 __global__ __launch_bounds__(256) void k_quant_kv(
     const uint16_t* __restrict__ k, Strides sk, const uint16_t* __restrict__ v, Strides sv,
-    int H, int N, int64_t npad, const uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
+    int H, int N, int64_t npad, uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_f8,
     uint16_t* __restrict__ v16) {
   constexpr int TPR = D / 8;
@@ -231,7 +240,32 @@ __global__ __launch_bounds__(256) void k_quant_kv(
   load_block<RPT, 1>(k + (int64_t)b * sk.b + (int64_t)h * sk.h + 8 * cg, sk.n, tok0, 0, N, kw);
   load_block<RPT, 1>(v + (int64_t)b * sv.b + (int64_t)h * sv.h + 8 * cg, sv.n, tok0, 0, N, vw);
   float mu[8], inv[8];
-  bf16x8_to_f32(*(const uint4*)(k_mean + bh * D + 8 * cg), mu);
+  if constexpr (KBM) {
+    __shared__ double bsum[RPI][D];
+    __shared__ __attribute__((aligned(16))) uint16_t bmean[D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double acc = 0.0;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        acc += (double)bf16_bits_to_f32(((const uint16_t*)&kw[i])[j]);   // rows >= N read as 0
+      bsum[r][8 * cg + j] = acc;
+    }
+    __syncthreads();
+    if (t < D) {
+      double acc = 0.0;
+#pragma unroll
+      for (int i = 0; i < RPI; ++i) acc += bsum[i][t];
+      const int nvalid = min(kQuantBlock, N - row0);    // <= 0 for an all-padding block
+      const uint16_t m16 = nvalid > 0 ? (uint16_t)f32_to_bf16_rne((float)(acc / (double)nvalid)) : 0;
+      bmean[t] = m16;
+      k_mean[(bh * nblk + blk) * D + t] = m16;
+    }
+    __syncthreads();
+    bf16x8_to_f32(*(const uint4*)(bmean + 8 * cg), mu);
+  } else {
+    bf16x8_to_f32(*(const uint4*)(k_mean + bh * D + 8 * cg), mu);
+  }
   if constexpr (!V16) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) inv[j] = v_inv[bh * D + 8 * cg + j];
@@ -333,25 +367,34 @@ __global__ void k_debug_e4m3(const float* __restrict__ x, uint8_t* __restrict__ 
   }
 }
 
-template <int D, bool V16, bool TOK>
+template <int D, bool V16, bool TOK, bool KBM>
 static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   const int per = stats_blocks_per_chunk(a.npad);
   const int chunks = stats_chunks(a.N);
-  hipLaunchKernelGGL((k_quant_q_stats<D, !V16, TOK>), dim3(chunks, a.H, a.B), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_quant_q_stats<D, !V16, TOK, !KBM>), dim3(chunks, a.H, a.B), dim3(256), 0, s,
                      a.q, a.sq, a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, per,
                      a.q_i8, a.q_scale, a.ksum_part, a.vmax_part);
-  hipLaunchKernelGGL((k_quant_finalize<D, !V16>), dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
-                     a.ksum_part, a.vmax_part, chunks, a.N, a.k_mean, a.v_scale, a.v_inv);
-  hipLaunchKernelGGL((k_quant_kv<D, V16, TOK>), dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
+  if constexpr (!V16 || !KBM)
+    hipLaunchKernelGGL((k_quant_finalize<D, !V16, !KBM>), dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
+                       a.ksum_part, a.vmax_part, chunks, a.N, a.k_mean, a.v_scale, a.v_inv);
+  hipLaunchKernelGGL((k_quant_kv<D, V16, TOK, KBM>), dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
                      a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, a.k_mean, a.v_inv,
                      a.k_i8, a.k_scale, a.v_f8, a.v16);
   return hipGetLastError();
 }
 
+template <int D, bool V16, bool TOK>
+static hipError_t launch_quant_kbm(const QuantArgs& a, hipStream_t s) {
+  if constexpr (!V16) {
+    if (a.kbm) return launch_quant_d<D, V16, TOK, true>(a, s);
+  }
+  return launch_quant_d<D, V16, TOK, false>(a, s);
+}
+
 template <int D>
 static hipError_t launch_quant_mode(const QuantArgs& a, hipStream_t s) {
-  if (a.pv == kPvBf16) return a.tok ? launch_quant_d<D, true, true>(a, s) : launch_quant_d<D, true, false>(a, s);
-  return a.tok ? launch_quant_d<D, false, true>(a, s) : launch_quant_d<D, false, false>(a, s);
+  if (a.pv == kPvBf16) return a.tok ? launch_quant_kbm<D, true, true>(a, s) : launch_quant_kbm<D, true, false>(a, s);
+  return a.tok ? launch_quant_kbm<D, false, true>(a, s) : launch_quant_kbm<D, false, false>(a, s);
 }
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {

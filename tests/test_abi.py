@@ -133,10 +133,14 @@ def test_mode_entry_points_validate(lib):
     assert bf16 - base == B * H * N * d                  # the V region holds 2-byte values
     assert tok - base == 2 * 4 * B * H * (N - N // 64)   # two scale arrays grow to one per token
     n = ctypes.c_size_t()
-    assert lib.sage_workspace_bytes_ex(B, H, N, d, 4, ctypes.byref(n)) == -1 and "mode" in _err(lib)
+    assert lib.sage_workspace_bytes_ex(B, H, N, d, 8, ctypes.byref(n)) == -1 and "mode" in _err(lib)
+    # block-residual K: the k_mean region holds one mean per 64-token block
+    kbm = _capi.sage_workspace_bytes_ex(B, H, N, d, _capi.mode_bits(k_block_mean=True))
+    assert kbm - base == 2 * B * H * d * (N // 64 - 1)  # both sizes are multiples of 256 here
+    assert lib.sage_workspace_bytes_ex(B, H, N, d, 5, ctypes.byref(n)) == -2 and "FP8" in _err(lib)
     st = (sage_strides * 4)(*([_st(100 * 2 * 128, 128, 2 * 128)] * 4))
     # unknown mode bits are rejected before anything else
-    rc = lib.sage_attn_fwd_ex(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 8, None, W, 1 << 40)
+    rc = lib.sage_attn_fwd_ex(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st, 16, None, W, 1 << 40)
     assert rc == -1 and "mode" in _err(lib)
     # the quality mode needs its larger workspace
     lib.sage_workspace_bytes_ex(1, 2, 100, 128, 0, ctypes.byref(n))

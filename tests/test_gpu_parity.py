@@ -256,3 +256,50 @@ def test_per_token_quality_mode_meets_rel_l2_gate_on_tiny():
     out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv="bf16", per_token=True)
     exact = oracle.attention_exact(_np(q), _np(k), _np(v))
     assert oracle.rel_l2(to_np(out), exact) <= 0.01
+
+
+
+# ---- block-residual K (FP8 P.V) ----
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["block64", "per_token"])
+@pytest.mark.parametrize("case", CASES[:6] + CASES[7:9], ids=_case_id)
+def test_block_mean_mode_matches_oracle(case, per_token):
+    B, N, H, d, seed, outl = case
+    print(f"[block-mean per_token={per_token}] {_case_id(case)}", flush=True)
+    q, k, v = random_qkv(B, N, H, d, seed, outl)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    mode = sage.mode_bits("fp8", per_token=per_token, k_block_mean=True)
+    ref = oracle.quantize(_np(q), _np(k), _np(v), block=1 if per_token else 64, k_block_mean=True)
+    gq = sage.sage_quant_qk_ex(qc, kc, vc, mode)
+    torch.cuda.synchronize()
+    nb = -(-N // 64)
+    km = gq["k_mean"].float().cpu().numpy()                   # [B, H, Npad/64, d]
+    assert np.array_equal(km[:, :, :nb].view(np.uint32), ref["k_bmean"].view(np.uint32)), "block means differ"
+    assert not km[:, :, nb:].any()
+    for name in ("q", "k"):
+        codes = gq[f"{name}_i8"].cpu().numpy()
+        assert np.array_equal(codes[:, :, :N], ref[f"{name}_i8"]), f"{name}_i8 differs"
+        sc = gq[f"{name}_scale"].cpu().numpy()
+        nsc = N if per_token else nb
+        assert np.array_equal(sc[:, :, :nsc].view(np.uint32), ref[f"{name}_scale"].view(np.uint32)), f"{name}_scale differs"
+    out = sage.sage_attn_fwd_ex(qc, kc, vc, per_token=per_token, k_block_mean=True)
+    o = to_np(out)
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE, quant=ref)
+    err = check_attention(o, pipe, f"block-mean {_case_id(case)}")
+    exact = oracle.attention_exact(_np(q), _np(k), _np(v))
+    assert oracle.rel_l2(o, exact) <= oracle.rel_l2(pipe, exact) + 0.002
+    print(f"    max|gpu-pipe| = {err:.2e}  relL2(gpu, exact) = {oracle.rel_l2(o, exact):.4f}", flush=True)
+
+
+def test_block_mean_mode_block_constant_keys():
+    # keys constant inside each 64-token block: K' = 0, the logits come only from the
+    # block-mean products
+    B, N, H, d = 1, 300, 2, 128
+    q, k, v = random_qkv(B, N, H, d, seed=41)
+    for j in range(0, N, 64):
+        k[:, j:j + 64] = k[:, j:j + 1]
+    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), k_block_mean=True)
+    ref = oracle.quantize(_np(q), _np(k), _np(v), k_block_mean=True)
+    assert not ref["k_i8"].any()
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE, quant=ref)
+    check_attention(to_np(out), pipe, "block-constant keys")
