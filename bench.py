@@ -321,7 +321,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(r["attn_tops"] / PEAK_TOPS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "kernel": "k_attn<%d, 0, false>" % w.d,
+                     "kernel": "k_attn<%d, 0, false, false>" % w.d,
                      "algorithmic_bytes": 5 * w.B * w.H * w.N * w.d},
         "sweep": sweep,
         "modes": quality,
