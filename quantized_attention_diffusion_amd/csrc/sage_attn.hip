@@ -518,6 +518,13 @@ __device__ __forceinline__ void block_mean_terms(const uint8_t* kbm_lds, const v
   for (int gq = 0; gq < G; ++gq) e[gq] = acc[gq][0] * qf[gq];
 }
 
+// A wave raises its issue priority while it issues a run of matrix-core instructions,
+// so that on a SIMD shared with a wave in its softmax the matrix core is fed first and
+// the softmax's VALU work fills the cycles the products take (measured: +3% at 4.6K and
+// 16K keys, neutral at 64K).
+__device__ __forceinline__ void mfma_priority_on() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_priority_off() { __builtin_amdgcn_s_setprio(0); }
+
 // Maps the linear workgroup id to (head, query block) so that the workgroups one XCD
 // receives (ids x, x+8, x+16, ... go to XCD x) are consecutive query blocks of the same
 // heads and share that head's K/V tiles in the XCD's L2.
@@ -684,11 +691,15 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
       if (t + kStages - 2 < ntiles) tile_barrier<KEEP>();
       else tile_barrier<0>();
       copy_tile(t + kStages - 1);        // into the stage all waves finished in step t-1
+      mfma_priority_on();
       qk_tile<D>(ring.kbuf(t), qfr, lo, S);
+      mfma_priority_off();
       softmax_step(t, false);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
+      mfma_priority_on();
       pv_tile<D>(ring.vbuf(t), P, lo, acc);
+      mfma_priority_off();
     }
     if (nfull < ntiles) {                // last tile: keys >= N masked
       tile_barrier<0>();
@@ -720,14 +731,18 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
       tile_barrier<0>();
       dma16.issue_v(v_rsrc, t * kKvTile * 2, vbuf, wave);
       copy_k(t + 1);
+      mfma_priority_on();
       qk_tile<D>(kbuf(t), qfr, lo, S);
+      mfma_priority_off();
       softmax_step(t, masked);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
       // V(t) must have landed; the copies of tile t+1 (K and key scales) may be in flight
       if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW + SIDE>();
       else tile_barrier<0>();
+      mfma_priority_on();
       pv_tile16<D>(vbuf, P, lo16, acc);
+      mfma_priority_off();
     };
     for (int t = 0; t < nfull; ++t) step(t, false);
     if (nfull < ntiles) step(nfull, true);
