@@ -347,25 +347,35 @@ template <int PV, bool BM = false>
 __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G], float log2_pscale,
                                              float (&m)[G], float (&lpart)[G], PTile<PV> (&P)[G],
                                              float (&alpha)[G], const float (&e)[G]) {
+  // integer row maximum: two chains of three-input maxima (16 per group)
   int xmi[G];
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
-    int a0 = max(max(S[gq][0][0], S[gq][0][1]), max(S[gq][0][2], S[gq][0][3]));
-    int a1 = max(max(S[gq][1][0], S[gq][1][1]), max(S[gq][1][2], S[gq][1][3]));
+    int a0 = max(S[gq][0][0], S[gq][0][1]);
+    int a1 = max(S[gq][1][0], S[gq][1][1]);
+    a0 = max(max(a0, S[gq][0][2]), S[gq][0][3]);
+    a1 = max(max(a1, S[gq][1][2]), S[gq][1][3]);
 #pragma unroll
-    for (int kt = 2; kt < 8; kt += 2) {
-      a0 = max(a0, max(max(S[gq][kt][0], S[gq][kt][1]), max(S[gq][kt][2], S[gq][kt][3])));
-      a1 = max(a1, max(max(S[gq][kt + 1][0], S[gq][kt + 1][1]), max(S[gq][kt + 1][2], S[gq][kt + 1][3])));
-    }
+    for (int kt = 2; kt < 8; kt += 2)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        a0 = max(max(a0, S[gq][kt][i]), S[gq][kt][i + 1]);
+        a1 = max(max(a1, S[gq][kt + 1][i]), S[gq][kt + 1][i + 1]);
+      }
     xmi[gq] = max(a0, a1);
   }
-  float nb[G], m_new[G];
+  float nb[G], m_new[G], sl[G];
+  static_assert(G == 2, "the lane-group reduction below pairs the two query groups");
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
     // c >= 0 and rounding is monotone: this is the max of fp32(x * c) (+ e) over the keys
     const float xs = (float)xmi[gq] * c[gq];
-    const float sl = max_over_lane_groups(BM ? xs + e[gq] : xs);
-    m_new[gq] = fmaxf(m[gq], sl);
+    sl[gq] = BM ? xs + e[gq] : xs;
+  }
+  max_over_lane_groups_pair(sl[0], sl[1]);
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) {
+    m_new[gq] = max2_nan_free(m[gq], sl[gq]);
     nb[gq] = BM ? e[gq] + (log2_pscale - m_new[gq]) : log2_pscale - m_new[gq];
     alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
   }
@@ -422,12 +432,16 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const v4f (&ks)
       }
     ym[gq] = fmaxf(a0, a1);
   }
-  float nb[G], m_new[G];
+  float nb[G], m_new[G], sl[G];
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
     const float ys = ym[gq] * qf[gq];
-    const float sl = max_over_lane_groups(ym[gq] == -INFINITY ? -INFINITY : (BM ? ys + e[gq] : ys));
-    m_new[gq] = fmaxf(m[gq], sl);
+    sl[gq] = ym[gq] == -INFINITY ? -INFINITY : (BM ? ys + e[gq] : ys);
+  }
+  max_over_lane_groups_pair(sl[0], sl[1]);
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) {
+    m_new[gq] = max2_nan_free(m[gq], sl[gq]);
     nb[gq] = BM ? e[gq] + (log2_pscale - m_new[gq]) : log2_pscale - m_new[gq];
     alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
   }

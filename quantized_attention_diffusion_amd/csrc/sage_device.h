@@ -46,6 +46,22 @@ __device__ __forceinline__ float max_over_lane_groups(float x) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// The maxima of two values (one per query group) over the 4 lane groups, in 7
+// instructions for both: swapping a's upper half against b's lower half leaves lanes
+// 0-31 holding a's and lanes 32-63 holding b's lane pairs (l, l^32), so one reduction
+// serves both; a final swap broadcasts each half.  (The attention kernel is compiled
+// without NaN semantics, so these maxima are single v_max_f32.)
+__device__ __forceinline__ float max2_nan_free(float x, float y) { return fmaxf(x, y); }
+__device__ __forceinline__ void max_over_lane_groups_pair(float& a, float& b) {
+  const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float r1 = max2_nan_free(__uint_as_float(s1[0]), __uint_as_float(s1[1]));
+  const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(r1), __float_as_uint(r1), false, false);
+  const float r2 = max2_nan_free(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
+  const auto s3 = __builtin_amdgcn_permlane32_swap(__float_as_uint(r2), __float_as_uint(r2), false, false);
+  a = __uint_as_float(s3[0]);
+  b = __uint_as_float(s3[1]);
+}
+
 __device__ __forceinline__ float sum_over_lane_groups(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
