@@ -27,7 +27,8 @@ SWEEP_STEPS = 20          # timed steps per sweep workload
 COPY_BYTES = 1 << 30      # calibration copy of the counter runs
 ATTN_SOURCES = ["quantized_attention_diffusion_amd/csrc/sage_attn.hip",
                 "quantized_attention_diffusion_amd/csrc/sage_device.h",
-                "quantized_attention_diffusion_amd/csrc/sage_internal.h"]
+                "quantized_attention_diffusion_amd/csrc/sage_internal.h",
+                "quantized_attention_diffusion_amd/build.py"]          # its compiler flags
 
 
 def _parse():
@@ -193,8 +194,8 @@ def cpu_baseline(w, rows_total: int = 3072):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources that define the attention kernel; a recorded traffic
-    figure is used only while it matches."""
+    """Hash of the sources and build flags that define the attention kernel; a recorded
+    traffic figure is used only while it matches."""
     import hashlib
 
     h = hashlib.sha256()
