@@ -7,6 +7,12 @@
 // to bf16, V unquantised) on bf16 matrix cores (the quality-first setting of the same
 // bjdmk page, section 4.3).
 //
+// Options (template parameters, chosen by the mode bits of the C ABI): PV = FP8 or bf16
+// P.V; TOK = one Q/K scale per token (the tile's key scales are staged in LDS with the
+// K tile); KBM = block-residual K (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 1:
+// the tile's two bf16 block means are staged with the K tile, and their products with
+// the query codes, on bf16 matrix cores, enter the logits).
+//
 // Work decomposition
 //   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 2 groups of 16
 //   queries; 2 workgroups per CU (2 waves per SIMD).  Keys are visited in tiles of 128.
