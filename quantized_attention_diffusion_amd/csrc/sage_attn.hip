@@ -207,18 +207,30 @@ __device__ __forceinline__ v8i load_vfrag(const uint8_t* vbuf, int dt, const Lan
   return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Exact int32 S^T of both query groups for a staged key tile (each K operand feeds both
-// groups): S[gq][kt] register i = S(query r of group gq, tile key 32g + 4kt + i).
+// The attention kernel starts its int32 S accumulators at kSBiasBits instead of 0.  The
+// products are bounded, |S| <= d * 127^2 < 2^21, so S + kSBiasBits is the bit pattern of
+// the float S + 1.5 * 2^23, which lies in [2^23, 2^24) where floats are the integers;
+// subtracting 1.5 * 2^23 then yields fp32(S) exactly.  One full-rate add replaces the
+// int-to-float conversion, which issues at a quarter of the VALU rate.  The biased
+// values keep the order of the integers, so maxima may still be taken on them.
+constexpr int kSBiasBits = 0x4B400000;
+constexpr float kSBias = 12582912.0f;                // 1.5 * 2^23
+static_assert(128 * 127 * 127 < (1 << 21), "S + 1.5 * 2^23 must stay in [2^23, 2^24)");
+
+__device__ __forceinline__ float s_to_f32(int biased) { return __builtin_bit_cast(float, biased) - kSBias; }
+
+// int32 S^T of both query groups for a staged key tile, plus s0 (each K operand feeds
+// both groups): S[gq][kt] register i = s0 + S(query r of group gq, tile key 32g + 4kt + i).
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const v4i (&qfr)[G][D / 64],
-                                        const LaneOffsets<D>& lo, v4i (&S)[G][8]) {
+                                        const LaneOffsets<D>& lo, v4i (&S)[G][8], int s0) {
 #pragma unroll
   for (int q = 0; q < 8 * (D / 64); ++q) {
     const int kt = q / (D / 64), kk = q % (D / 64);
     const v4i a = load_kfrag<D>(kbuf, q, lo);
 #pragma unroll
     for (int gq = 0; gq < G; ++gq)
-      S[gq][kt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qfr[gq][kk], kk == 0 ? v4i{0, 0, 0, 0} : S[gq][kt], 0, 0, 0);
+      S[gq][kt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qfr[gq][kk], kk == 0 ? v4i{s0, s0, s0, s0} : S[gq][kt], 0, 0, 0);
   }
 }
 
@@ -284,8 +296,8 @@ __device__ __forceinline__ void pv_tile16(const uint8_t* vbuf, const PTile<kPvBf
 }
 
 // Online-softmax update of one 16-query group for one tile, not interleaved (used at the
-// ends of the pipeline and for the ragged last tile).  S is consumed (converted to fp32
-// exactly: |S| < 2^24); c = fp32(q factor * k_scale) of this lane's keys.  Produces the
+// ends of the pipeline and for the ragged last tile).  S holds biased accumulators
+// (s_to_f32 recovers fp32(S) exactly); c = fp32(q factor * k_scale) of this lane's keys.  Produces the
 // P operand, updates the running max m and this lane's partial row sum, and
 // returns alpha = 2^(m_old - m_new), the factor the accumulators need.  When MASKED,
 // keys at tile index >= nvalid are removed by giving them the logit -inf; a lane whose
@@ -298,7 +310,7 @@ __device__ __forceinline__ float softmax_group(v4i (&S)[8], float c, int nvalid,
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xf[kt][i] = (float)S[kt][i];
+    for (int i = 0; i < 4; ++i) xf[kt][i] = s_to_f32(S[kt][i]);
   if constexpr (MASKED) {
     const int nv = nvalid - 32 * g;                // valid keys among this lane's 32
     const bool zero_c = (c == 0.0f);
@@ -346,7 +358,7 @@ __device__ __forceinline__ void rescale(v4f (&acc)[D / 16], float alpha) {
 }
 
 // Online-softmax update of both query groups for one full tile (no masking): integer
-// row max (exact, no NaN handling), fp32 conversion (exact: |S| < 2^24), exp2 of the
+// row max of the biased S (exact, no NaN handling), exact fp32 S by s_to_f32, exp2 of the
 // fused multiply-add, rounding into P, independent partial row sums.  Same
 // arithmetic as softmax_group<false>; the two groups' work is interleaved for ILP.
 template <int PV, bool BM = false>
@@ -375,7 +387,7 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
     // c >= 0 and rounding is monotone: this is the max of fp32(x * c) (+ e) over the keys
-    const float xs = (float)xmi[gq] * c[gq];
+    const float xs = s_to_f32(xmi[gq]) * c[gq];
     sl[gq] = BM ? xs + e[gq] : xs;
   }
   max_over_lane_groups_pair(sl[0], sl[1]);
@@ -392,7 +404,7 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
     for (int gq = 0; gq < G; ++gq) {
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[gq][kt][i], c[gq], nb[gq]));
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_to_f32(S[gq][kt][i]), c[gq], nb[gq]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
       store_p<PV>(P[gq], kt, p);
@@ -410,7 +422,7 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
 //
 // Online-softmax update of both query groups with per-token scales: ks[kt][i] is the
 // scale of tile key 32g + 4kt + i and qf the query factor fp32(q_scale * sm_scale *
-// log2 e).  y = fp32(S * ks) per key; the row maximum is the max of fp32(y * qf) (qf >= 0
+// log2 e).  y = fp32(S * ks) per key (S from the biased accumulators by s_to_f32); the row maximum is the max of fp32(y * qf) (qf >= 0
 // and rounding is monotone, so it is fp32(max y * qf)); p = exp2(fma(y, qf, nb)).  When
 // MASKED, keys at tile index >= nvalid get p = 0 and take no part in the maximum.
 template <int PV, bool MASKED, bool BM = false>
@@ -425,7 +437,7 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const v4f (&ks)
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[gq][kt][i] = (float)S[gq][kt][i] * ks[kt][i];
+      for (int i = 0; i < 4; ++i) y[gq][kt][i] = s_to_f32(S[gq][kt][i]) * ks[kt][i];
     float a0 = -INFINITY, a1 = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 8; kt += 2)
@@ -712,7 +724,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
       else tile_barrier<0>();
       copy_tile(t + kStages - 1);        // into the stage all waves finished in step t-1
       mfma_priority_on();
-      qk_tile<D>(ring.kbuf(t), qfr, lo, S);
+      qk_tile<D>(ring.kbuf(t), qfr, lo, S, kSBiasBits);
       mfma_priority_off();
       softmax_step(t, false);
 #pragma unroll
@@ -723,7 +735,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
     }
     if (nfull < ntiles) {                // last tile: keys >= N masked
       tile_barrier<0>();
-      qk_tile<D>(ring.kbuf(nfull), qfr, lo, S);
+      qk_tile<D>(ring.kbuf(nfull), qfr, lo, S, kSBiasBits);
       softmax_step(nfull, true);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
@@ -752,7 +764,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
       dma16.issue_v(v_rsrc, t * kKvTile * 2, vbuf, wave);
       copy_k(t + 1);
       mfma_priority_on();
-      qk_tile<D>(kbuf(t), qfr, lo, S);
+      qk_tile<D>(kbuf(t), qfr, lo, S, kSBiasBits);
       mfma_priority_off();
       softmax_step(t, masked);
 #pragma unroll
@@ -812,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
   load_q<D>(q_i8 + bh * npad * D, qrow0, lane, qfr);
   __syncthreads();
   v4i S[G][8];
-  qk_tile<D>(klds, qfr, LaneOffsets<D>(lane), S);
+  qk_tile<D>(klds, qfr, LaneOffsets<D>(lane), S, 0);
   const int64_t ld = (int64_t)n_kv_tiles * kKvTile;
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
