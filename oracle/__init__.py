@@ -18,6 +18,9 @@ What the oracle computes, and where each step comes from:
   fp32 online softmax in base 2 over key tiles (the blockwise computation of the
   bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2), P rounded
   to FP8 e4m3, PV accumulated, normalised at the end.
+* ``select_tiles`` (module ``sparse``) - block-sparse attention: the key tiles each
+  query block keeps for a density tau (the sd114.wiki ComfyUI-sol-attn page, 核心亮点
+  item 4, names tau and its sparse-to-dense schedule; the selection rule is a reading).
 
 Points the pages leave open are fixed by readings that are listed in the module
 docstrings.  Everything is numpy; floating point is fp64 except where the method's
@@ -29,6 +32,7 @@ from .quant import (QUANT_BLOCK, bf16_round, k_token_mean, quantize_int8_blocks,
                     quantize_v_fp8, quantize)
 from .attention import (LOG2E, attention_exact, qk_int32, attention_pipeline,
                         default_sm_scale, rel_l2)
+from .sparse import SPARSE_TILE, keep_count, block_code_sums, tile_importance, select_tiles
 
 __all__ = [
     "e4m3_decode", "e4m3_encode", "e4m3_table", "E4M3_MAX",
@@ -36,4 +40,5 @@ __all__ = [
     "quantize_v_fp8", "quantize",
     "LOG2E", "attention_exact", "qk_int32", "attention_pipeline",
     "default_sm_scale", "rel_l2",
+    "SPARSE_TILE", "keep_count", "block_code_sums", "tile_importance", "select_tiles",
 ]

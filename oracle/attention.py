@@ -148,7 +148,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                        quant=None, int8_qk: bool = True, fp8_p: bool = True,
                        fp8_v: bool = True, smooth_k: bool = True,
                        bf16_p: bool = False, block: int = QUANT_BLOCK,
-                       k_block_mean: bool = False) -> np.ndarray:
+                       k_block_mean: bool = False, tiles=None) -> np.ndarray:
     """Quantised attention.  q, k, v: float32 [B, N, H, d] holding bf16 values.
 
     ``quant``: the dict of :func:`oracle.quantize` if already computed.  ``rows``:
@@ -159,6 +159,10 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     ``fp8_v=False`` this is the quality mode (INT8 QK^T, bf16 P.V).  ``block``: tokens
     per Q/K scale when ``quant`` is not given (``quant`` carries its own); 1 selects
     per-token scales and their decision arithmetic.
+    ``tiles``: block-sparse attention (``oracle.sparse``); tiles[b][h][I] lists, in
+    ascending order, the key tiles of ``kv_tile`` keys that query block I (rows
+    I*kv_tile ...) visits.  None visits every tile.
+    The keys are those of ``quant`` (their count may differ from the queries').
     Returns fp64 [B, R, H, d]."""
     if fp8_p and bf16_p:
         raise ValueError("P is rounded either to e4m3 or to bf16, not both")
@@ -172,6 +176,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     qb = int(quant.get("block", QUANT_BLOCK))
     kbm = quant.get("k_bmean")                       # [B, H, nblk, d] or None
     r = _rows(N, rows)
+    Nk = int(quant["k_i8"].shape[2]) if int8_qk else k.shape[1]
     L = F32(sm * LOG2E)
     out = np.empty((B, len(r), H, d), dtype=np.float64)
     T = int(kv_tile)
@@ -185,11 +190,16 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                 vs = np.ones(d)
             if int8_qk:
                 kq = quant["k_i8"][b, h]
-                ks = quant["k_scale"][b, h][np.arange(N) // qb]                 # [N]
+                ks = quant["k_scale"][b, h][np.arange(Nk) // qb]                # [Nk]
             else:
                 kf = k[b, :, h, :].astype(np.float64)
-            for c0 in range(0, len(r), 256):
-                rr = r[c0:c0 + 256]
+            if tiles is None:
+                chunks = [np.arange(c0, min(len(r), c0 + 256)) for c0 in range(0, len(r), 256)]
+            else:
+                qblk = r // T
+                chunks = [np.nonzero(qblk == I)[0] for I in np.unique(qblk)]
+            for pos in chunks:
+                rr = r[pos]
                 R = len(rr)
                 if int8_qk:
                     S = qk_int32(quant["q_i8"][b, h][rr], kq)                 # [R, N]
@@ -200,7 +210,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                         Dq = (quant["q_i8"][b, h][rr].astype(np.float64) @
                               kbm[b, h].astype(np.float64).T).astype(F32)      # [R, nblk]
                         E = (Dq.astype(np.float64) * qf[:, None]).astype(F32)
-                        ek = E[:, np.arange(N) // QUANT_BLOCK]                # [R, N]
+                        ek = E[:, np.arange(Nk) // QUANT_BLOCK]               # [R, Nk]
                     else:
                         ek = None
                 else:
@@ -208,8 +218,10 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                 m = np.full(R, -np.inf, dtype=F32)
                 l = np.zeros(R)
                 acc = np.zeros((R, d))
-                for t0 in range(0, N, T):
-                    t1 = min(N, t0 + T)
+                starts = (range(0, Nk, T) if tiles is None
+                          else [int(J) * T for J in tiles[b][h][int(rr[0]) // T]])
+                for t0 in starts:
+                    t1 = min(Nk, t0 + T)
                     if int8_qk and qb > 1:
                         x = S[:, t0:t1]
                         c = (qf[:, None] * ks[None, t0:t1]).astype(F32)       # [R, t]
@@ -247,7 +259,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                     l = alpha * l + p.astype(np.float64).sum(axis=1)
                     acc = alpha[:, None] * acc + pq @ vv[t0:t1]
                     m = m_new
-                out[b, c0:c0 + R, h, :] = acc * vs[None, :] / l[:, None]
+                out[b, pos, h, :] = acc * vs[None, :] / l[:, None]
     return out
 
 
