@@ -196,6 +196,48 @@ int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
                      void* workspace, size_t workspace_bytes);
 
 /*
+ * Block-sparse attention over key tiles.  The sd114.wiki page "ComfyUI-sol-attn"
+ * (核心亮点, item 4) runs its sparse attention with a value tau that moves over the
+ * sampling steps, sparse early and dense late, and gives no rule for which blocks to
+ * skip.  Here tau is the density: each block of 128 queries keeps
+ * k = max(1, min(T, ceil(tau * T))) of the T key tiles of 128 keys, those of largest
+ * importance, the lower tile index winning ties.  The importance of tile J for query
+ * block I is the mean, over their valid (query, key) pairs, of q_scale * k_scale * S,
+ * computed exactly from the per-channel sums A_a, B_b of the INT8 codes of each
+ * 64-token scale block a of I and b of J, in fp64 with every operation rounded once:
+ * t_ab = (qs_a * ks_b) * <A_a, B_b>, importance = ((t_00 + t_01) + (t_10 + t_11)) /
+ * (n_I * n_J) (a scale block past the last token gives t = 0).  The kept tiles are
+ * visited in ascending order with the arithmetic of sage_attn_fwd_prequant; tau >= 1
+ * gives exactly the dense result.  Limits: Npad/128 <= SAGE_MAX_SPARSE_TILES and
+ * B*H <= 65535 (else SAGE_EUNSUPPORTED); tau must be > 0 (else SAGE_EINVAL).
+ *
+ * sage_select_scratch_bytes - scratch size of sage_block_select.  After the call the
+ *   scratch holds the code sums, int32 [2][B][H][Npad/64][d] (Q then K), and from the
+ *   next 256-byte boundary the fp64 importance matrix [B][H][Npad/128][Npad/128].
+ * sage_block_select - the kept tiles from the quantised operands of sage_quant_qk
+ *   (mode 0, device pointers, 256-byte aligned): tile_count [B][H][Npad/128] int32
+ *   (k in every entry) and tile_list [B][H][Npad/128][Npad/128] int32, whose rows
+ *   start with the k kept tile indices in ascending order (the rest of each row is
+ *   not written).  Asynchronous on `stream`; the outputs must not overlap the inputs
+ *   or the scratch.
+ * sage_workspace_bytes_sparse / sage_attn_fwd_sparse - sage_attn_fwd with the tile
+ *   selection between the quantisation and the attention.  The workspace holds the
+ *   mode-0 layout of sage_attn_fwd, then the selection scratch, tile_count and
+ *   tile_list, each region starting on a 256-byte boundary.
+ */
+#define SAGE_MAX_SPARSE_TILES 4096
+int sage_select_scratch_bytes(int B, int H, int N, int d, size_t* bytes);
+int sage_block_select(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                      const float* k_scale, int B, int H, int N, int d, float density,
+                      int32_t* tile_count, int32_t* tile_list, void* scratch,
+                      size_t scratch_bytes, void* stream);
+int sage_workspace_bytes_sparse(int B, int H, int N, int d, size_t* bytes);
+int sage_attn_fwd_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                         int B, int H, int N, int d, float sm_scale,
+                         const sage_strides strides[4], float density, void* stream,
+                         void* workspace, size_t workspace_bytes);
+
+/*
  * sage_debug_qk_i32 - diagnostic: the exact int32 S = Q8.K8^T tiles of head (b, h),
  * computed by the same staging and matrix-core code as the attention kernel.
  * Covers query rows [q_block*block_m, (q_block+n_q_blocks)*block_m) and keys

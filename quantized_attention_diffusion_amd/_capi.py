@@ -24,7 +24,9 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_EINVAL", -2: "SAGE_EUNSUPPORTED", -3: "SAGE_EA
 EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
            "sage_quant_scratch_bytes", "sage_workspace_bytes", "sage_workspace_bytes_ex",
            "sage_quant_qk", "sage_quant_qk_ex", "sage_attn_fwd_prequant", "sage_attn_fwd",
-           "sage_attn_fwd_ex", "sage_debug_qk_i32", "sage_debug_e4m3"]
+           "sage_attn_fwd_ex", "sage_select_scratch_bytes", "sage_block_select",
+           "sage_workspace_bytes_sparse", "sage_attn_fwd_sparse", "sage_debug_qk_i32",
+           "sage_debug_e4m3"]
 
 SAGE_PV_FP8, SAGE_PV_BF16, SAGE_QK_PER_TOKEN, SAGE_K_BLOCK_MEAN = 0, 1, 2, 4
 
@@ -77,6 +79,11 @@ _SIGS = {
                            ctypes.POINTER(sage_strides), _P, _P, _SZ]),
     "sage_attn_fwd_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
                               ctypes.POINTER(sage_strides), _I, _P, _P, _SZ]),
+    "sage_select_scratch_bytes": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "sage_block_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "sage_workspace_bytes_sparse": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "sage_attn_fwd_sparse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
+                                  ctypes.POINTER(sage_strides), ctypes.c_float, _P, _P, _SZ]),
     "sage_debug_qk_i32": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "sage_debug_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
 }
@@ -287,6 +294,70 @@ def sage_attn_fwd_ex(q, k, v, out: torch.Tensor | None = None, sm_scale: float |
     else:
         _check(load().sage_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                        B, H, N, d, sm, strides, mode, _stream(dev),
+                                       workspace.data_ptr(), workspace.numel()))
+    return out
+
+
+def sage_select_scratch_bytes(B: int, H: int, N: int, d: int) -> int:
+    n = _SZ()
+    _check(load().sage_select_scratch_bytes(B, H, N, d, ctypes.byref(n)))
+    return n.value
+
+
+def sage_workspace_bytes_sparse(B: int, H: int, N: int, d: int) -> int:
+    n = _SZ()
+    _check(load().sage_workspace_bytes_sparse(B, H, N, d, ctypes.byref(n)))
+    return n.value
+
+
+def sage_block_select(quant: dict, density: float, return_importance: bool = False):
+    """Kept key tiles of every query block for ``density`` from the operands of
+    :func:`sage_quant_qk`: (tile_count int32 [B, H, nqb], tile_list int32 [B, H, nqb, T]
+    whose rows start with the tile_count kept tiles in ascending order), plus the fp64
+    importance matrix [B, H, nqb, T] from the scratch with ``return_importance``."""
+    B, H, npad, d = quant["q_i8"].shape
+    N = int(quant["N"])
+    dev = quant["q_i8"].device
+    nt = npad // sage_kernel_info()["kv_tile"]
+    count = torch.zeros((B, H, nt), dtype=torch.int32, device=dev)
+    lists = torch.full((B, H, nt, nt), -1, dtype=torch.int32, device=dev)
+    scratch = torch.empty(sage_select_scratch_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    _check(load().sage_block_select(
+        quant["q_i8"].data_ptr(), quant["q_scale"].data_ptr(), quant["k_i8"].data_ptr(),
+        quant["k_scale"].data_ptr(), B, H, N, d, float(density), count.data_ptr(), lists.data_ptr(),
+        scratch.data_ptr(), scratch.numel(), _stream(dev)))
+    if not return_importance:
+        return count, lists
+    sums_bytes = -(-2 * B * H * (npad // 64) * d * 4 // 256) * 256
+    imp = scratch[sums_bytes:sums_bytes + B * H * nt * nt * 8].view(torch.float64).reshape(B, H, nt, nt)
+    return count, lists, imp
+
+
+def sage_attn_fwd_sparse(q, k, v, density: float, out: torch.Tensor | None = None,
+                         sm_scale: float | None = None, layout: str = "bnhd",
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Block-sparse sage_attn_fwd: each block of 128 queries visits the key tiles of
+    largest importance, a fraction ``density`` of them (1 gives the dense result)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _bf16_cuda(n, t)
+    (B, H, N, d), sq = _dims(q, layout)
+    dk, sk = _dims(k, layout)
+    dv, sv = _dims(v, layout)
+    if dk != (B, H, N, d) or dv != (B, H, N, d):
+        raise ValueError("q, k and v must have the same shape")
+    dev = q.device
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    _bf16_cuda("out", out)
+    do, so = _dims(out, layout)
+    if do != (B, H, N, d):
+        raise ValueError("out must have the shape of q")
+    if workspace is None:
+        workspace = torch.empty(sage_workspace_bytes_sparse(B, H, N, d), dtype=torch.uint8, device=dev)
+    sm = _default_scale(d) if sm_scale is None else float(sm_scale)
+    strides = (sage_strides * 4)(sq, sk, sv, so)
+    _check(load().sage_attn_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, H, N, d, sm, strides, float(density), _stream(dev),
                                        workspace.data_ptr(), workspace.numel()))
     return out
 

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage_attn.so")
-SOURCES = ["sage_api.hip", "sage_quant.hip", "sage_attn.hip"]
+SOURCES = ["sage_api.hip", "sage_quant.hip", "sage_attn.hip", "sage_select.hip"]
 # The attention kernel never forms a NaN (masked keys take -inf logits and p = 0, zero
 # scales are handled explicitly), so its maxima need no NaN-quieting instructions.
 EXTRA = {"sage_attn.hip": ["-fno-honor-nans"]}

@@ -13,6 +13,8 @@
 
 #define SAGE_EXPORT extern "C" __attribute__((visibility("default")))
 
+static_assert(SAGE_MAX_SPARSE_TILES == sage::kMaxSparseTiles, "header and kernel limits agree");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -130,6 +132,42 @@ void carve_scratch(char*& p, const QuantLayout& L, sage::QuantArgs& a) {
   a.ksum_part = (double*)p; p += round_up(L.ksum, kAlign);
   a.vmax_part = (float*)p;  p += round_up(L.vmax, kAlign);
   a.v_inv = (float*)p;      p += round_up(L.vinv, kAlign);
+}
+
+// Block-sparse selection: code sums, importance matrix, and the kept-tile lists.
+struct SelectLayout {
+  int nt;                              // key tiles (= query blocks) per head
+  size_t sums, imp, count, list;       // sizes in bytes
+};
+
+SelectLayout select_layout(int B, int H, int N, int d) {
+  SelectLayout S;
+  const int64_t npad = sage::padded_tokens(N);
+  const size_t bh = (size_t)B * H;
+  S.nt = (int)(npad / sage::kKvTile);
+  S.sums = 2 * bh * (npad / sage::kQuantBlock) * d * sizeof(int32_t);
+  S.imp = bh * S.nt * S.nt * sizeof(double);
+  S.count = bh * S.nt * sizeof(int32_t);
+  S.list = bh * S.nt * S.nt * sizeof(int32_t);
+  return S;
+}
+
+size_t select_scratch_size(const SelectLayout& S) { return round_up(S.sums, kAlign) + round_up(S.imp, kAlign); }
+
+int check_sparse(int B, int H, int N, int d, float density) {
+  if (int rc = check_shape(B, H, N, d)) return rc;
+  if (isnan(density) || !(density > 0.0f)) return fail(SAGE_EINVAL, "density must be > 0 (got %g)", (double)density);
+  if ((int64_t)B * H > 65535) return fail(SAGE_EUNSUPPORTED, "block-sparse attention needs B*H <= 65535");
+  if (sage::padded_tokens(N) / sage::kKvTile > sage::kMaxSparseTiles)
+    return fail(SAGE_EUNSUPPORTED, "block-sparse attention supports at most %d key tiles (N=%d)",
+                sage::kMaxSparseTiles, N);
+  return SAGE_OK;
+}
+
+// k = max(1, min(T, ceil(density * T))), exact in fp64 for an fp32 density.
+int keep_count(float density, int nt) {
+  const double k = ceil((double)density * (double)nt);
+  return (int)std::max(1.0, std::min((double)nt, k));
 }
 
 sage::Strides to_internal(const sage_strides& s) { return sage::Strides{s.b, s.h, s.n}; }
@@ -287,11 +325,16 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
   return launch_status(sage::launch_attn(a, (hipStream_t)stream), "attention");
 }
 
-SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
-                                 int B, int H, int N, int d, float sm_scale,
-                                 const sage_strides strides[4], int mode, void* stream,
-                                 void* workspace, size_t workspace_bytes) {
+// The whole path; with `sparse` the tile selection runs between the quantisation and
+// the attention, on the selection region that follows the mode-0 layout.
+static int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                         int B, int H, int N, int d, float sm_scale,
+                         const sage_strides strides[4], int mode, bool sparse, float density,
+                         void* stream, void* workspace, size_t workspace_bytes) {
   if (int rc = check_mode(mode)) return rc;
+  if (sparse) {
+    if (int rc = check_sparse(B, H, N, d, density)) return rc;
+  }
   if (!strides) return fail(SAGE_EINVAL, "strides is NULL");
   if (int rc = validate_quant_inputs(q, k, v, &strides[0], &strides[1], &strides[2], B, H, N, d)) return rc;
   if (int rc = check_view("out", out, &strides[3], B, H, N, d)) return rc;
@@ -305,7 +348,9 @@ SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uin
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale))
     return fail(SAGE_EINVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
   const QuantLayout L = layout(B, H, N, d, mode);
-  const size_t need = workspace_size(L);
+  const SelectLayout SL = select_layout(B, H, N, d);
+  const size_t need = workspace_size(L) +
+      (sparse ? select_scratch_size(SL) + round_up(SL.count, kAlign) + round_up(SL.list, kAlign) : 0);
   if (!workspace) return fail(SAGE_EWORKSPACE, "workspace is NULL");
   if (!aligned(workspace, kAlign)) return fail(SAGE_EWORKSPACE, "workspace is not 256-byte aligned");
   if (workspace_bytes < need)
@@ -344,7 +389,95 @@ SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uin
   a.B = B; a.H = H; a.N = N; a.d = d; a.npad = L.npad;
   a.log2e_scale = log2e_scale(sm_scale);
   a.log2_pscale = log2_pscale();
+  if (sparse) {
+    sage::SelectArgs sa;
+    sa.q_i8 = qa.q_i8; sa.k_i8 = qa.k_i8; sa.q_scale = qa.q_scale; sa.k_scale = qa.k_scale;
+    sa.B = B; sa.H = H; sa.N = N; sa.d = d; sa.npad = L.npad;
+    sa.keep = keep_count(density, SL.nt);
+    sa.sums = (int32_t*)p;      p += round_up(SL.sums, kAlign);
+    sa.imp = (double*)p;        p += round_up(SL.imp, kAlign);
+    sa.tile_count = (int32_t*)p; p += round_up(SL.count, kAlign);
+    sa.tile_list = (int32_t*)p;  p += round_up(SL.list, kAlign);
+    if (int rc = launch_status(sage::launch_block_select(sa, s), "tile selection")) return rc;
+    a.tile_count = sa.tile_count;
+    a.tile_list = sa.tile_list;
+    a.tiles_max = SL.nt;
+  }
   return launch_status(sage::launch_attn(a, s), "attention");
+}
+
+SAGE_EXPORT int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                                 int B, int H, int N, int d, float sm_scale,
+                                 const sage_strides strides[4], int mode, void* stream,
+                                 void* workspace, size_t workspace_bytes) {
+  return attn_fwd_impl(q, k, v, out, B, H, N, d, sm_scale, strides, mode, false, 1.0f, stream,
+                       workspace, workspace_bytes);
+}
+
+SAGE_EXPORT int sage_workspace_bytes_sparse(int B, int H, int N, int d, size_t* bytes) {
+  if (!bytes) return fail(SAGE_EINVAL, "bytes is NULL");
+  if (int rc = check_sparse(B, H, N, d, 1.0f)) return rc;
+  const SelectLayout SL = select_layout(B, H, N, d);
+  *bytes = workspace_size(layout(B, H, N, d)) + select_scratch_size(SL) + round_up(SL.count, kAlign) +
+           round_up(SL.list, kAlign);
+  return ok();
+}
+
+SAGE_EXPORT int sage_attn_fwd_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                                     int B, int H, int N, int d, float sm_scale,
+                                     const sage_strides strides[4], float density, void* stream,
+                                     void* workspace, size_t workspace_bytes) {
+  return attn_fwd_impl(q, k, v, out, B, H, N, d, sm_scale, strides, 0, true, density, stream,
+                       workspace, workspace_bytes);
+}
+
+SAGE_EXPORT int sage_select_scratch_bytes(int B, int H, int N, int d, size_t* bytes) {
+  if (!bytes) return fail(SAGE_EINVAL, "bytes is NULL");
+  if (int rc = check_sparse(B, H, N, d, 1.0f)) return rc;
+  *bytes = select_scratch_size(select_layout(B, H, N, d));
+  return ok();
+}
+
+SAGE_EXPORT int sage_block_select(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                  const float* k_scale, int B, int H, int N, int d, float density,
+                                  int32_t* tile_count, int32_t* tile_list, void* scratch,
+                                  size_t scratch_bytes, void* stream) {
+  if (int rc = check_sparse(B, H, N, d, density)) return rc;
+  const QuantLayout L = layout(B, H, N, d);
+  const SelectLayout SL = select_layout(B, H, N, d);
+  const void* ins[4] = {q_i8, q_scale, k_i8, k_scale};
+  const char* in_names[4] = {"q_i8", "q_scale", "k_i8", "k_scale"};
+  const size_t in_sizes[4] = {L.q_i8, L.q_scale, L.k_i8, L.k_scale};
+  for (int i = 0; i < 4; ++i) {
+    if (!ins[i]) return fail(SAGE_EINVAL, "%s is NULL", in_names[i]);
+    if (!aligned(ins[i], kAlign)) return fail(SAGE_EALIGN, "%s is not 256-byte aligned", in_names[i]);
+  }
+  if (!tile_count || !tile_list) return fail(SAGE_EINVAL, "tile_count and tile_list must not be NULL");
+  if (!aligned(tile_count, 4) || !aligned(tile_list, 4)) return fail(SAGE_EALIGN, "tile_count/tile_list not 4-byte aligned");
+  const Extent outs[2] = {{(uintptr_t)tile_count, (uintptr_t)tile_count + SL.count},
+                          {(uintptr_t)tile_list, (uintptr_t)tile_list + SL.list}};
+  if (overlaps(outs[0], outs[1])) return fail(SAGE_EINVAL, "tile_count overlaps tile_list");
+  const size_t need = select_scratch_size(SL);
+  if (!scratch) return fail(SAGE_EWORKSPACE, "scratch is NULL");
+  if (!aligned(scratch, kAlign)) return fail(SAGE_EWORKSPACE, "scratch is not 256-byte aligned");
+  if (scratch_bytes < need) return fail(SAGE_EWORKSPACE, "scratch has %zu bytes, %zu needed", scratch_bytes, need);
+  const Extent es{(uintptr_t)scratch, (uintptr_t)scratch + need};
+  for (int i = 0; i < 2; ++i) {
+    if (overlaps(outs[i], es)) return fail(SAGE_EINVAL, "tile lists overlap the scratch");
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], Extent{(uintptr_t)ins[j], (uintptr_t)ins[j] + in_sizes[j]}))
+        return fail(SAGE_EINVAL, "tile lists overlap %s", in_names[j]);
+  }
+  sage::SelectArgs sa;
+  sa.q_i8 = q_i8; sa.k_i8 = k_i8; sa.q_scale = q_scale; sa.k_scale = k_scale;
+  sa.B = B; sa.H = H; sa.N = N; sa.d = d; sa.npad = L.npad;
+  sa.keep = keep_count(density, SL.nt);
+  char* p = (char*)scratch;
+  sa.sums = (int32_t*)p; p += round_up(SL.sums, kAlign);
+  sa.imp = (double*)p;
+  sa.tile_count = tile_count;
+  sa.tile_list = tile_list;
+  return launch_status(sage::launch_block_select(sa, (hipStream_t)stream), "tile selection");
 }
 
 SAGE_EXPORT int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,

@@ -606,9 +606,12 @@ struct AttnSmem {
 // TOK: per-token Q/K scales (q_scale, k_scale [B][H][Npad]); the key scales of each
 // tile are staged in LDS with the K tile.  KBM: block-residual K; the block means of
 // each tile are staged likewise and their products with the query codes are added to
-// the logits.
-template <int D, int PV, bool TOK, bool KBM>
-__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a) {
+// the logits.  SPARSE: the workgroup visits only the key tiles its query block keeps
+// (a.tile_list, ascending), with the same per-tile arithmetic; the masked last tile
+// is visited only if it is kept.
+template <int D, int PV, bool TOK, bool KBM, bool SPARSE>
+__device__ __forceinline__ void attn_body(const AttnArgs& a) {
+  static_assert(!SPARSE || (PV == kPvFp8 && !TOK && !KBM), "block-sparse visits: FP8 P.V, 64-token scales");
   using Smem = AttnSmem<D, PV, TOK, KBM>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Smem::BYTES];
   uint8_t* const ksmem = smem + Smem::MAIN;
@@ -704,42 +707,60 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
   };
 
   if constexpr (PV == kPvFp8) {
+    // visit i (LDS stage i % kStages) processes key tile tile_at(i): every tile in
+    // order, or the query block's kept tiles
+    int nvis = ntiles;
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const_i32_ptr kept = nullptr;
+    if constexpr (SPARSE) {
+      const int64_t row = bh * nqb + qb;
+      nvis = __builtin_amdgcn_readfirstlane(((const_i32_ptr)a.tile_count)[row]);
+      kept = (const_i32_ptr)a.tile_list + row * a.tiles_max;
+    }
+    auto tile_at = [&](int i) -> int {
+      if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(kept[i]);
+      else return i;
+    };
+    const bool last_masked = nfull < ntiles && tile_at(nvis - 1) == ntiles - 1;
+    const int nfull_vis = last_masked ? nvis - 1 : nvis;   // visits without masking
     const Ring<D> ring{smem};
     const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(a.v_f8 + bh * D * a.npad, (int64_t)D * a.npad);
-    auto copy_tile = [&](int t) {
-      if (t < ntiles) {
-        dma.issue_k(k_rsrc, t * kKvTile * D, ring.kbuf(t), wave);
-        dma.issue_v(v_rsrc, t * kKvTile, ring.vbuf(t), wave);
+    auto copy_tile = [&](int i) {
+      if (i < nvis) {
+        const int t = tile_at(i);
+        dma.issue_k(k_rsrc, t * kKvTile * D, ring.kbuf(i), wave);
+        dma.issue_v(v_rsrc, t * kKvTile, ring.vbuf(i), wave);
         copy_ks(t);
       }
     };
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t) copy_tile(t);
+    for (int i = 0; i < kStages - 1; ++i) copy_tile(i);
     load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
     init_state();
     constexpr int KEEP = (kStages - 2) * (DmaOffsets<D>::PER_TILE + SIDE);
-    for (int t = 0; t < nfull; ++t) {
-      // tile t has landed once only the copies of the kStages-2 later tiles may be in flight
-      if (t + kStages - 2 < ntiles) tile_barrier<KEEP>();
+    for (int i = 0; i < nfull_vis; ++i) {
+      // visit i has landed once only the copies of the kStages-2 later visits may be in flight
+      if (i + kStages - 2 < nvis) tile_barrier<KEEP>();
       else tile_barrier<0>();
-      copy_tile(t + kStages - 1);        // into the stage all waves finished in step t-1
+      copy_tile(i + kStages - 1);        // into the stage all waves finished in visit i-1
       mfma_priority_on();
-      qk_tile<D>(ring.kbuf(t), qfr, lo, S, kSBiasBits);
+      qk_tile<D>(ring.kbuf(i), qfr, lo, S, kSBiasBits);
       mfma_priority_off();
-      softmax_step(t, false);
+      softmax_step(tile_at(i), false);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
       mfma_priority_on();
-      pv_tile<D>(ring.vbuf(t), P, lo, acc);
+      pv_tile<D>(ring.vbuf(i), P, lo, acc);
       mfma_priority_off();
     }
-    if (nfull < ntiles) {                // last tile: keys >= N masked
+    if (last_masked) {                   // last tile: keys >= N masked
+      const int i = nvis - 1;
       tile_barrier<0>();
-      qk_tile<D>(ring.kbuf(nfull), qfr, lo, S, kSBiasBits);
-      softmax_step(nfull, true);
+      qk_tile<D>(ring.kbuf(i), qfr, lo, S, kSBiasBits);
+      softmax_step(ntiles - 1, true);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
-      pv_tile<D>(ring.vbuf(nfull), P, lo, acc);
+      pv_tile<D>(ring.vbuf(i), P, lo, acc);
     }
   } else {
     // K double-buffered, one bf16 V buffer.  Step t: barrier (K(t) landed, every wave
@@ -805,6 +826,16 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a)
   }
 }
 
+template <int D, int PV, bool TOK, bool KBM>
+__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a) {
+  attn_body<D, PV, TOK, KBM, false>(a);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn_sparse(AttnArgs a) {
+  attn_body<D, kPvFp8, false, false, true>(a);
+}
+
 // Int32 S tiles through the same staging (LDS DMA, swizzle) and matrix-core code as
 // k_attn.
 template <int D>
@@ -856,6 +887,10 @@ static void launch_attn_tok(const AttnArgs& a, unsigned grid, hipStream_t s) {
 
 template <int D>
 static void launch_attn_d(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if (a.tile_list) {
+    hipLaunchKernelGGL(k_attn_sparse<D>, dim3(grid), dim3(kThreads), 0, s, a);
+    return;
+  }
   if (a.pv == kPvBf16) launch_attn_tok<D, kPvBf16>(a, grid, s);
   else launch_attn_tok<D, kPvFp8>(a, grid, s);
 }
@@ -895,6 +930,8 @@ template __global__ void k_attn<128, kPvFp8, false, true>(AttnArgs);
 template __global__ void k_attn<128, kPvFp8, true, true>(AttnArgs);
 template __global__ void k_attn<128, kPvBf16, false, false>(AttnArgs);
 template __global__ void k_attn<128, kPvBf16, true, false>(AttnArgs);
+template __global__ void k_attn_sparse<64>(AttnArgs);
+template __global__ void k_attn_sparse<128>(AttnArgs);
 template __global__ void k_debug_qk<64>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,
                                         int64_t, int, int, int, int32_t* __restrict__);
 template __global__ void k_debug_qk<128>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,

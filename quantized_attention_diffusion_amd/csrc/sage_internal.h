@@ -17,6 +17,7 @@ constexpr int kStages = 2;          // LDS stages (K tile + V tile) of the atten
 constexpr int kMinWavesPerSimd = 2; // occupancy the attention kernel is compiled for
 constexpr float kPScale = 448.0f;   // static scale of P before e4m3 rounding
 constexpr int kMaxStatsChunks = 128; // partial-statistics rows per (b, h) in the quantisation pass
+constexpr int kMaxSparseTiles = 4096; // key tiles per head of the block-sparse path (LDS of the selection)
 
 // Precision of the P.V product: P in e4m3 with per-channel e4m3 V (speed), or P in
 // bf16 with the unquantised bf16 V (quality).
@@ -79,10 +80,29 @@ struct AttnArgs {
   int64_t npad;
   float log2e_scale;   // fp32(sm_scale * log2(e))
   float log2_pscale;   // fp32(log2(448))
+  // block-sparse: kept key tiles per (b, h, query block) and their ascending indices
+  // [B][H][Npad/128][tiles_max]; null for the dense kernel
+  const int32_t* tile_count = nullptr;
+  const int32_t* tile_list = nullptr;
+  int tiles_max = 0;
+};
+
+// Operands of the block-sparse tile selection.
+struct SelectArgs {
+  const int8_t *q_i8, *k_i8;
+  const float *q_scale, *k_scale;   // [B][H][Npad/64]
+  int B, H, N, d;
+  int64_t npad;
+  int keep;                         // tiles kept per query block
+  int32_t* sums;                    // scratch [2][B*H][Npad/64][d]: per-block code sums of Q, K
+  double* imp;                      // scratch [B*H][Npad/128][Npad/128]: tile importance
+  int32_t* tile_count;              // [B*H][Npad/128]
+  int32_t* tile_list;               // [B*H][Npad/128][Npad/128]
 };
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_block_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_t npad,
                            int64_t bh, int q_block, int kv_tile, int n_q_blocks,
                            int n_kv_tiles, int32_t* s_out, hipStream_t s);

@@ -155,6 +155,46 @@ def test_mode_entry_points_validate(lib):
     assert rc == -1 and "mode" in _err(lib)
 
 
+def test_sparse_entry_points_validate(lib):
+    from quantized_attention_diffusion_amd import _capi
+    from quantized_attention_diffusion_amd._capi import sage_strides
+    B, H, N, d = 1, 24, 4608, 128
+    nt = N // 128
+    n = ctypes.c_size_t()
+    # scratch: Q and K code sums per 64-token block (int32) + the fp64 importance matrix
+    assert lib.sage_select_scratch_bytes(B, H, N, d, ctypes.byref(n)) == 0
+    assert n.value == 2 * B * H * (N // 64) * d * 4 + B * H * nt * nt * 8
+    # the sparse workspace appends the scratch, tile_count and tile_list to the mode-0 one
+    extra = _capi.sage_workspace_bytes_sparse(B, H, N, d) - _capi.sage_workspace_bytes(B, H, N, d)
+    r256 = lambda x: -(-x // 256) * 256
+    assert extra == n.value + r256(B * H * nt * 4) + r256(B * H * nt * nt * 4)
+    # limits: key tiles per head, B*H
+    assert lib.sage_select_scratch_bytes(1, 1, 4096 * 128 + 1, 64, ctypes.byref(n)) == -2
+    assert "key tiles" in _err(lib)
+    assert lib.sage_workspace_bytes_sparse(300, 300, 1024, 64, ctypes.byref(n)) == -2
+    st = (sage_strides * 4)(*([_st(100 * 2 * 128, 128, 2 * 128)] * 4))
+    for bad in (0.0, -1.0, float("nan")):
+        rc = lib.sage_attn_fwd_sparse(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st,
+                                      ctypes.c_float(bad), None, W, 1 << 40)
+        assert rc == -1 and "density" in _err(lib)
+        rc = lib.sage_block_select(A, A + (1 << 20), B_, B_ + (1 << 20), 1, 2, 100, 128, ctypes.c_float(bad),
+                                   C, C + (1 << 20), W, 1 << 30, None)
+        assert rc == -1 and "density" in _err(lib)
+    # the dense workspace is too small for the sparse call
+    rc = lib.sage_attn_fwd_sparse(A, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.088), st,
+                                  ctypes.c_float(0.5), None, W, _capi.sage_workspace_bytes(1, 2, 100, 128))
+    assert rc == -4 and "needed" in _err(lib)
+    rc = lib.sage_block_select(A, A + (1 << 20), B_, B_ + (1 << 20), 1, 2, 100, 128, ctypes.c_float(0.5),
+                               0, C, W, 1 << 30, None)
+    assert rc == -1 and "tile_count" in _err(lib)
+    rc = lib.sage_block_select(A, A + (1 << 20), B_, B_ + (1 << 20), 1, 2, 100, 128, ctypes.c_float(0.5),
+                               C, C + 4096, W, 16, None)
+    assert rc == -4 and "needed" in _err(lib)
+    rc = lib.sage_block_select(A, A + (1 << 20), B_, B_ + (1 << 20), 1, 2, 100, 128, ctypes.c_float(0.5),
+                               A + 64, C, W, 1 << 30, None)
+    assert rc == -1 and "overlap" in _err(lib)
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from quantized_attention_diffusion_amd import _capi
     monkeypatch.setattr(_capi, "_lib", None)
