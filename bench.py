@@ -84,6 +84,43 @@ def measure_mode(w, steps, warmup, **opts):
     return {"N": w.N, "ms_per_step": round(ms, 4), "tops": round(w.ops / (ms * 1e-3) / 1e12, 2)}
 
 
+# densities of the block-sparse path that the bench times (whole step)
+SPARSE_DENSITIES = (0.5, 0.25)
+
+
+def measure_sparse(w, steps, warmup, density):
+    """Whole-step time of sage_attn_fwd_sparse at ``density`` on workload w.  ``tops`` is
+    dense-equivalent (4*B*H*N^2*d over the step time); ``kept`` is the fraction of key
+    tiles each query block visits and ``tops_executed`` counts only those."""
+    import math
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_qkv(w))
+    out = torch.empty_like(q)
+    ws = torch.empty(sage.sage_workspace_bytes_sparse(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        sage.sage_attn_fwd_sparse(q, k, v, density, out=out, workspace=ws)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        sage.sage_attn_fwd_sparse(q, k, v, density, out=out, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    nt = sage.sage_padded_tokens(w.N) // sage.sage_kernel_info()["kv_tile"]
+    kept = max(1, min(nt, math.ceil(density * nt))) / nt
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return {"N": w.N, "density": density, "kept": round(kept, 4), "ms_per_step": round(ms, 4),
+            "tops": round(w.ops / (ms * 1e-3) / 1e12, 2),
+            "tops_executed": round(kept * w.ops / (ms * 1e-3) / 1e12, 2)}
+
+
 def measure(w, steps, warmup):
     import torch
     import workloads
@@ -295,6 +332,8 @@ def main():
             print(f"[bench] optional modes {name} N={wq.N}", file=sys.stderr, flush=True)
             st, wu = (args.steps, args.warmup) if name == w.name else (SWEEP_STEPS, 2)
             quality[name] = {mname: measure_mode(wq, st, wu, **opts) for mname, opts in MODES.items()}
+            for dens in SPARSE_DENSITIES:
+                quality[name][f"sparse_{dens}"] = measure_sparse(wq, st, wu, dens)
     print(f"[bench] {w.name} B={w.B} H={w.H} N={w.N} d={w.d}: {args.warmup} warmup + {args.steps} steps",
           file=sys.stderr, flush=True)
     r = measure(w, args.steps, args.warmup)
