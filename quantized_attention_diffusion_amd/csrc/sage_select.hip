@@ -13,11 +13,13 @@
 // the integer dot products are exact in int64), so any implementation that follows
 // the formula takes the same decisions.  Ties go to the lower tile index.
 //
-// Three kernels: code sums per 64-token block (reads the INT8 operands once), the
+// Three kernels: code sums per 64-token block (reads the INT8 operands once); the
 // importance matrix of each head (8 query blocks x 32 key tiles per workgroup, code
-// sums staged in LDS), and the selection of each query block by exact ranks (rank of J
-// = tiles more important than J, or as important with a lower index; kept iff
-// rank < k), compacted in ascending tile order with a workgroup prefix sum.
+// sums staged in LDS as int16 pairs for v_dot2_i32_i16); and the selection of each
+// query block by exact ranks (rank of J = tiles more important than J, or as important
+// with a lower index; kept iff rank < k), compacted in ascending tile order with a
+// workgroup prefix sum.  (A bitonic sort in LDS measured slower: its barrier per stage
+// costs more than the independent rank loops at 36 and 512 tiles.)
 #include "sage_internal.h"
 
 namespace sage {
@@ -64,46 +66,63 @@ __global__ __launch_bounds__(kSelThreads) void k_block_sums(const int8_t* __rest
 }
 
 // imp[bh][I][J] for I in [8*blockIdx.y, +8) and J in [32*blockIdx.x, +32): thread
-// (i = t / 32, j = t % 32).
+// (i = t / 32, j = t % 32).  A code sum is at most 64 * 127 = 8128 in magnitude, so the
+// sums are staged as int16 channel pairs and the dot products run on v_dot2_i32_i16:
+// 16 products (each below 2^26) per int32 partial, the partials summed in int64.
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void k_tile_importance(const int32_t* __restrict__ sums,
                                                                 const float* __restrict__ q_scale,
                                                                 const float* __restrict__ k_scale,
                                                                 int N, int64_t npad, int64_t n_bh,
                                                                 double* __restrict__ imp) {
-  constexpr int P = D + 1;                     // LDS row pitch in words (odd: no bank conflicts)
-  __shared__ int qa[kImpQb * kTilesPerBlock][P];
-  __shared__ int kb[kImpKt * kTilesPerBlock][P];
+  constexpr int W = D / 2;                     // int16 pairs per row
+  constexpr int P = W + 4;                     // LDS row pitch in words (16-byte aligned rows)
+  static_assert(kQuantBlock * 127 < 32768, "code sums fit int16");
+  __shared__ __attribute__((aligned(16))) int qa[kImpQb * kTilesPerBlock][P];
+  __shared__ __attribute__((aligned(16))) int kb[kImpKt * kTilesPerBlock][P];
   const int64_t bh = blockIdx.z, nblk = npad / kQuantBlock;
   const int nt = (int)(npad / kKvTile);
   const int I0 = blockIdx.y * kImpQb, J0 = blockIdx.x * kImpKt;
   const int32_t* qs_sums = sums + bh * nblk * D;
   const int32_t* ks_sums = sums + (n_bh + bh) * nblk * D;
+  auto pack = [](int2 x) { return (x.x & 0xffff) | (x.y << 16); };
   // stage the code sums of the 16 query and 64 key scale blocks (zeros past the end)
-  for (int e = threadIdx.x; e < kImpQb * kTilesPerBlock * D; e += kSelThreads) {
-    const int row = e / D, c = e % D;
+  for (int e = threadIdx.x; e < kImpQb * kTilesPerBlock * W; e += kSelThreads) {
+    const int row = e / W, w = e % W;
     const int64_t blk = (int64_t)I0 * kTilesPerBlock + row;
-    qa[row][c] = blk < nblk ? qs_sums[blk * D + c] : 0;
+    qa[row][w] = blk < nblk ? pack(*(const int2*)(qs_sums + blk * D + 2 * w)) : 0;
   }
-  for (int e = threadIdx.x; e < kImpKt * kTilesPerBlock * D; e += kSelThreads) {
-    const int row = e / D, c = e % D;
+  for (int e = threadIdx.x; e < kImpKt * kTilesPerBlock * W; e += kSelThreads) {
+    const int row = e / W, w = e % W;
     const int64_t blk = (int64_t)J0 * kTilesPerBlock + row;
-    kb[row][c] = blk < nblk ? ks_sums[blk * D + c] : 0;
+    kb[row][w] = blk < nblk ? pack(*(const int2*)(ks_sums + blk * D + 2 * w)) : 0;
   }
   __syncthreads();
   const int i = threadIdx.x / kImpKt, j = threadIdx.x % kImpKt;
   const int I = I0 + i, J = J0 + j;
   if (I >= nt || J >= nt) return;
+  typedef short v2s __attribute__((ext_vector_type(2)));
   double tab[kTilesPerBlock][kTilesPerBlock];
 #pragma unroll
   for (int a = 0; a < kTilesPerBlock; ++a) {
 #pragma unroll
     for (int b = 0; b < kTilesPerBlock; ++b) {
       const int64_t ablk = (int64_t)I * kTilesPerBlock + a, bblk = (int64_t)J * kTilesPerBlock + b;
-      int64_t dot = 0;
       const int* x = qa[i * kTilesPerBlock + a];
       const int* y = kb[j * kTilesPerBlock + b];
-      for (int c = 0; c < D; ++c) dot += (int64_t)x[c] * y[c];
+      int64_t dot = 0;
+#pragma unroll
+      for (int w0 = 0; w0 < W; w0 += 8) {
+        const int4 x0 = *(const int4*)(x + w0), x1 = *(const int4*)(x + w0 + 4);
+        const int4 y0 = *(const int4*)(y + w0), y1 = *(const int4*)(y + w0 + 4);
+        const int xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const int ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        int part = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          part = __builtin_amdgcn_sdot2(__builtin_bit_cast(v2s, xs[u]), __builtin_bit_cast(v2s, ys[u]), part, false);
+        dot += part;
+      }
       tab[a][b] = (ablk < nblk && bblk < nblk)
                       ? ((double)q_scale[bh * nblk + ablk] * (double)k_scale[bh * nblk + bblk]) * (double)dot
                       : 0.0;
