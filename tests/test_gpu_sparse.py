@@ -15,6 +15,8 @@ from gpu_helpers import require_gpu, to_np, random_qkv, check_attention
 pytestmark = pytest.mark.gpu
 
 CASES = [  # (B, N, H, d, seed, outliers)
+    (1, 1, 1, 128, 1, 0),       # one tile of one key
+    (1, 129, 2, 64, 6, 0),      # last tile of one key
     (1, 256, 2, 64, 0, 0),      # the 'tiny' workload shape: 2 tiles
     (1, 1000, 2, 128, 8, 4),    # ragged last tile of 104 keys, outlier channels
     (2, 700, 3, 64, 3, 0),      # last tile of 60 keys; its second scale block lies past N
