@@ -7,7 +7,9 @@
  * section 一), the K mean term kept in bf16 and only the remainder quantised
  * (sd114.wiki page on ComfyUI-sol-attn, "核心亮点" item 1), computed block by block
  * without materialising the N x N score matrix (bjdmk page
- * "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2).
+ * "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2).  Options: bf16 P.V,
+ * per-token scales and block-residual K (sage_attn_fwd_ex), and block-sparse key tiles
+ * chosen by a density (sage_attn_fwd_sparse; sd114.wiki page, "核心亮点" item 4).
  *
  * Conventions shared by every entry point
  * ---------------------------------------

@@ -11,7 +11,10 @@
 // P.V; TOK = one Q/K scale per token (the tile's key scales are staged in LDS with the
 // K tile); KBM = block-residual K (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 1:
 // the tile's two bf16 block means are staged with the K tile, and their products with
-// the query codes, on bf16 matrix cores, enter the logits).
+// the query codes, on bf16 matrix cores, enter the logits).  The block-sparse kernel
+// (k_attn_sparse) is the FP8 body visiting only the key tiles its query block keeps
+// (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 4; the selection is in
+// sage_select.hip).
 //
 // Work decomposition
 //   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 2 groups of 16
@@ -30,6 +33,8 @@
 //   Row j of key sub-tile kt is mapped to tile key 32*(j/4) + 4*kt + j%4, so lane l ends
 //   up holding, for its query r, the 32 consecutive tile keys 32g .. 32g+31 (register i
 //   of sub-tile kt = key 32g + 4kt + i).  Those 32 keys lie in one 64-key scale block.
+//   The int32 accumulators start at 0x4B400000 (s_to_f32 recovers fp32(S) with one
+//   exact subtraction).
 //   O^T = V^T . P^T with v_mfma_f32_16x16x128_f8f6f4 (speed): the column operand of
 //   lane l is 32 bytes of P for query r over keys 32g .. 32g+31, exactly the values the
 //   lane already holds, so P never leaves its registers; the row operand is 32 bytes of
