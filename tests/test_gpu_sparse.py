@@ -107,6 +107,10 @@ def test_sparse_layouts_and_workspace_reuse():
     for _ in range(2):
         o = sage.sage_attn_fwd_sparse(qh, kh, vh, 0.4, layout="bhnd", workspace=ws)
         assert torch.equal(o.transpose(1, 2).contiguous().view(torch.int16), ref.view(torch.int16))
+    # strided q/k/v slices of one fused [B, N, 3, H, d] projection output
+    qkv = torch.stack([qd, kd, vd], dim=2).contiguous()
+    o = sage.sage_attn_fwd_sparse(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], 0.4)
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
 
 
 @pytest.mark.parametrize("name,density,n_heads", [("flux_like", 0.3, 24), ("stress", 0.25, 2)])
