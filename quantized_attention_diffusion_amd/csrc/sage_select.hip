@@ -76,26 +76,35 @@ __global__ __launch_bounds__(kSelThreads) void k_tile_importance(const int32_t* 
                                                                 int N, int64_t npad, int64_t n_bh,
                                                                 double* __restrict__ imp) {
   constexpr int W = D / 2;                     // int16 pairs per row
-  constexpr int P = W + 4;                     // LDS row pitch in words (16-byte aligned rows)
+  constexpr int P = W + 4;                     // LDS row pitch of the query rows (16-byte aligned)
+  constexpr int CH = W / 4;                    // 16-byte chunks per key row
+  // Key rows are unpadded and their 16-byte chunks XOR-swizzled by key tile, so the 32
+  // tiles a wave reads at once spread over the banks (at most 2 lanes per bank group).
+  auto ksw = [](int row) { return (row / kTilesPerBlock) & (CH - 1); };
   static_assert(kQuantBlock * 127 < 32768, "code sums fit int16");
   __shared__ __attribute__((aligned(16))) int qa[kImpQb * kTilesPerBlock][P];
-  __shared__ __attribute__((aligned(16))) int kb[kImpKt * kTilesPerBlock][P];
+  __shared__ __attribute__((aligned(16))) int kb[kImpKt * kTilesPerBlock][W];
   const int64_t bh = blockIdx.z, nblk = npad / kQuantBlock;
   const int nt = (int)(npad / kKvTile);
   const int I0 = blockIdx.y * kImpQb, J0 = blockIdx.x * kImpKt;
   const int32_t* qs_sums = sums + bh * nblk * D;
   const int32_t* ks_sums = sums + (n_bh + bh) * nblk * D;
   auto pack = [](int2 x) { return (x.x & 0xffff) | (x.y << 16); };
-  // stage the code sums of the 16 query and 64 key scale blocks (zeros past the end)
+  // stage the code sums of the 16 query and 64 key scale blocks (zeros past the end);
+  // the trip counts are constants, so every load is issued before the first store
+  static_assert((kImpQb * kTilesPerBlock * W) % kSelThreads == 0 && (kImpKt * kTilesPerBlock * W) % kSelThreads == 0,
+                "whole staging passes");
+#pragma unroll
   for (int e = threadIdx.x; e < kImpQb * kTilesPerBlock * W; e += kSelThreads) {
     const int row = e / W, w = e % W;
     const int64_t blk = (int64_t)I0 * kTilesPerBlock + row;
     qa[row][w] = blk < nblk ? pack(*(const int2*)(qs_sums + blk * D + 2 * w)) : 0;
   }
+#pragma unroll
   for (int e = threadIdx.x; e < kImpKt * kTilesPerBlock * W; e += kSelThreads) {
     const int row = e / W, w = e % W;
     const int64_t blk = (int64_t)J0 * kTilesPerBlock + row;
-    kb[row][w] = blk < nblk ? pack(*(const int2*)(ks_sums + blk * D + 2 * w)) : 0;
+    kb[row][4 * ((w / 4) ^ ksw(row)) + w % 4] = blk < nblk ? pack(*(const int2*)(ks_sums + blk * D + 2 * w)) : 0;
   }
   __syncthreads();
   const int i = threadIdx.x / kImpKt, j = threadIdx.x % kImpKt;
@@ -109,12 +118,14 @@ __global__ __launch_bounds__(kSelThreads) void k_tile_importance(const int32_t* 
     for (int b = 0; b < kTilesPerBlock; ++b) {
       const int64_t ablk = (int64_t)I * kTilesPerBlock + a, bblk = (int64_t)J * kTilesPerBlock + b;
       const int* x = qa[i * kTilesPerBlock + a];
-      const int* y = kb[j * kTilesPerBlock + b];
+      const int yrow = j * kTilesPerBlock + b;
+      const int* y = kb[yrow];
       int64_t dot = 0;
 #pragma unroll
       for (int w0 = 0; w0 < W; w0 += 8) {
         const int4 x0 = *(const int4*)(x + w0), x1 = *(const int4*)(x + w0 + 4);
-        const int4 y0 = *(const int4*)(y + w0), y1 = *(const int4*)(y + w0 + 4);
+        const int4 y0 = *(const int4*)(y + 4 * ((w0 / 4) ^ ksw(yrow)));
+        const int4 y1 = *(const int4*)(y + 4 * ((w0 / 4 + 1) ^ ksw(yrow)));
         const int xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         const int ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
         int part = 0;
