@@ -137,3 +137,13 @@ def test_full_size_sparse(name, density, n_heads):
             pipe = oracle.attention_pipeline(qh, kh, vh, quant=ref, rows=rows, tiles=tiles)
             err = check_attention(to_np(out[:, rows, h:h + 1, :]), pipe, f"{name} head {h}")
             print(f"    head {h}: max|gpu-pipe| = {err:.2e}", flush=True)
+
+
+def test_sparse_with_a_given_sm_scale():
+    q, k, v = random_qkv(1, 700, 2, 64, 41, 0)
+    sm = 0.05
+    out = sage.sage_attn_fwd_sparse(q.cuda(), k.cuda(), v.cuda(), 0.5, sm_scale=sm)
+    ref = oracle.quantize(_np(q), _np(k), _np(v))
+    _, tiles = oracle.select_tiles(ref, 0.5)      # the selection does not depend on sm_scale
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), sm_scale=sm, quant=ref, tiles=tiles)
+    check_attention(to_np(out), pipe, "sparse sm_scale 0.05")
