@@ -31,6 +31,16 @@ ATTN_SOURCES = ["quantized_attention_diffusion_amd/csrc/sage_attn.hip",
                 "quantized_attention_diffusion_amd/build.py"]          # its compiler flags
 
 
+def attn_kernel_name(w, info):
+    """The attention kernel the library launches for workload w: the workgroup-pair
+    priority instance when the grid is at most two rounds of two workgroups per compute
+    unit, the plain one otherwise."""
+    import torch
+    grid = -(-w.N // info["block_m"]) * w.B * w.H
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return "k_attn<%d, 0, false, false, %s>" % (w.d, "true" if grid <= 4 * cus else "false")
+
+
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,7 +371,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(r["attn_tops"] / PEAK_TOPS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "kernel": "k_attn<%d, 0, false, false>" % w.d,
+                     "kernel": attn_kernel_name(w, info),
                      "algorithmic_bytes": 5 * w.B * w.H * w.N * w.d},
         "sweep": sweep,
         "modes": quality,

@@ -45,6 +45,7 @@
 //   Every per-query quantity (running max m, partial row sum, accumulators) is thus
 //   lane-local; only the tile maximum and the final row sum combine the 4 lanes
 //   r, r+16, r+32, r+48.
+#include <atomic>
 #include "sage_internal.h"
 #include "sage_device.h"
 
@@ -555,12 +556,39 @@ __device__ __forceinline__ void block_mean_terms(const uint8_t* kbm_lds, const v
   for (int gq = 0; gq < G; ++gq) e[gq] = acc[gq][0] * qf[gq];
 }
 
-// A wave raises its issue priority while it issues a run of matrix-core instructions,
-// so that on a SIMD shared with a wave in its softmax the matrix core is fed first and
-// the softmax's VALU work fills the cycles the products take (measured: +3% at 4.6K and
-// 16K keys, neutral at 64K).
-__device__ __forceinline__ void mfma_priority_on() { __builtin_amdgcn_s_setprio(1); }
-__device__ __forceinline__ void mfma_priority_off() { __builtin_amdgcn_s_setprio(0); }
+// Wave issue priorities.
+// - A wave raises its priority while it issues a run of matrix-core instructions, so
+//   that on a SIMD shared with a wave in its softmax the matrix core is fed first and the
+//   softmax's VALU work fills the cycles the products take (measured: +3% at 4.6K and
+//   16K keys, neutral at 64K).
+// - PAIR (chosen by the host when the grid is at most two rounds of two workgroups per
+//   CU): the base priority also evens out the two workgroups that share a CU.
+//   Workgroups are dispatched in id order, about one per CU for each group of cu_count
+//   consecutive ids, so in the first rounds a CU's two workgroups come from neighbouring
+//   groups and the later one is the younger. When waves of both are ready, a SIMD issues
+//   the older wave first; the younger workgroup then lags and runs its last tiles alone,
+//   at a lower rate, which in the last round leaves the CU's other slot idle. With PAIR,
+//   workgroups of odd groups take base priority 1, the others 0, and the matrix-core
+//   runs priority 2 (measured: +3% at 4.6K keys and 24 heads). The per-workgroup choice
+//   costs a branch at each switch, which measured 1-5% slower on long grids, where the
+//   pairs are no longer neighbours in id; those use the plain form.
+template <bool PAIR>
+struct IssuePriority {
+  int raised = 0;   // workgroup-uniform (scalar register)
+  __device__ __forceinline__ explicit IssuePriority(int cu_count) {
+    if constexpr (PAIR)
+      raised = __builtin_amdgcn_readfirstlane(((blockIdx.x / (unsigned)cu_count) & 1u) ? 1 : 0);
+  }
+  __device__ __forceinline__ void mfma() const { __builtin_amdgcn_s_setprio(PAIR ? 2 : 1); }
+  __device__ __forceinline__ void base() const {
+    if constexpr (PAIR) {
+      if (raised) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    } else {
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+};
 
 // Maps the linear workgroup id to (head, query block) so that the workgroups one XCD
 // receives (ids x, x+8, x+16, ... go to XCD x) are consecutive query blocks of the same
@@ -614,7 +642,7 @@ struct AttnSmem {
 // the logits.  SPARSE: the workgroup visits only the key tiles its query block keeps
 // (a.tile_list, ascending), with the same per-tile arithmetic; the masked last tile
 // is visited only if it is kept.
-template <int D, int PV, bool TOK, bool KBM, bool SPARSE>
+template <int D, int PV, bool TOK, bool KBM, bool SPARSE, bool PAIR>
 __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   static_assert(!SPARSE || (PV == kPvFp8 && !TOK && !KBM), "block-sparse visits: FP8 P.V, 64-token scales");
   using Smem = AttnSmem<D, PV, TOK, KBM>;
@@ -626,6 +654,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 
   // workgroup-uniform indices kept in scalar registers (readfirstlane), so that the
   // per-tile k_scale reads are scalar loads and never wait on the vector-memory counter
+  const IssuePriority<PAIR> prio(a.cu_count);
+  if constexpr (PAIR) prio.base();
   const int nqb = (int)(a.npad / kBlockM);
   const int total = nqb * a.B * a.H;
   const int work = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, total));
@@ -748,15 +778,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       if (i + kStages - 2 < nvis) tile_barrier<KEEP>();
       else tile_barrier<0>();
       copy_tile(i + kStages - 1);        // into the stage all waves finished in visit i-1
-      mfma_priority_on();
+      prio.mfma();
       qk_tile<D>(ring.kbuf(i), qfr, lo, S, kSBiasBits);
-      mfma_priority_off();
+      prio.base();
       softmax_step(tile_at(i), false);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
-      mfma_priority_on();
+      prio.mfma();
       pv_tile<D>(ring.vbuf(i), P, lo, acc);
-      mfma_priority_off();
+      prio.base();
     }
     if (last_masked) {                   // last tile: keys >= N masked
       const int i = nvis - 1;
@@ -789,18 +819,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       tile_barrier<0>();
       dma16.issue_v(v_rsrc, t * kKvTile * 2, vbuf, wave);
       copy_k(t + 1);
-      mfma_priority_on();
+      prio.mfma();
       qk_tile<D>(kbuf(t), qfr, lo, S, kSBiasBits);
-      mfma_priority_off();
+      prio.base();
       softmax_step(t, masked);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
       // V(t) must have landed; the copies of tile t+1 (K and key scales) may be in flight
       if (t + 1 < ntiles) tile_barrier<DmaOffsets<D>::KPW + SIDE>();
       else tile_barrier<0>();
-      mfma_priority_on();
+      prio.mfma();
       pv_tile16<D>(vbuf, P, lo16, acc);
-      mfma_priority_off();
+      prio.base();
     };
     for (int t = 0; t < nfull; ++t) step(t, false);
     if (nfull < ntiles) step(nfull, true);
@@ -831,14 +861,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   }
 }
 
-template <int D, int PV, bool TOK, bool KBM>
+template <int D, int PV, bool TOK, bool KBM, bool PAIR>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn(AttnArgs a) {
-  attn_body<D, PV, TOK, KBM, false>(a);
+  attn_body<D, PV, TOK, KBM, false, PAIR>(a);
 }
 
-template <int D>
+template <int D, bool PAIR>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn_sparse(AttnArgs a) {
-  attn_body<D, kPvFp8, false, false, true>(a);
+  attn_body<D, kPvFp8, false, false, true, PAIR>(a);
 }
 
 // Int32 S tiles through the same staging (LDS DMA, swizzle) and matrix-core code as
@@ -873,15 +903,29 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
   }
 }
 
+// Workgroup-pair issue priorities for grids of at most two rounds of two workgroups per
+// compute unit.
+static bool pair_priorities(const AttnArgs& a, unsigned grid) {
+  return grid <= 4u * (unsigned)a.cu_count;
+}
+
+template <int D, int PV, bool TOK, bool KBM>
+static void launch_attn_pair(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if (pair_priorities(a, grid))
+    hipLaunchKernelGGL((k_attn<D, PV, TOK, KBM, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn<D, PV, TOK, KBM, false>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
 template <int D, int PV, bool TOK>
 static void launch_attn_kbm(const AttnArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (PV == kPvFp8) {
     if (a.k_bmean) {
-      hipLaunchKernelGGL((k_attn<D, PV, TOK, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      launch_attn_pair<D, PV, TOK, true>(a, grid, s);
       return;
     }
   }
-  hipLaunchKernelGGL((k_attn<D, PV, TOK, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  launch_attn_pair<D, PV, TOK, false>(a, grid, s);
 }
 
 template <int D, int PV>
@@ -893,14 +937,33 @@ static void launch_attn_tok(const AttnArgs& a, unsigned grid, hipStream_t s) {
 template <int D>
 static void launch_attn_d(const AttnArgs& a, unsigned grid, hipStream_t s) {
   if (a.tile_list) {
-    hipLaunchKernelGGL(k_attn_sparse<D>, dim3(grid), dim3(kThreads), 0, s, a);
+    if (pair_priorities(a, grid))
+      hipLaunchKernelGGL((k_attn_sparse<D, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_sparse<D, false>), dim3(grid), dim3(kThreads), 0, s, a);
     return;
   }
   if (a.pv == kPvBf16) launch_attn_tok<D, kPvBf16>(a, grid, s);
   else launch_attn_tok<D, kPvFp8>(a, grid, s);
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+// Compute units of the current device, read once per device (the period of the
+// workgroup-pair priorities; any positive value gives the same results).
+static int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+hipError_t launch_attn(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  a.cu_count = device_cu_count();
   const int nqb = (int)(a.npad / kBlockM);
   const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.H);
   if (a.d == 64) launch_attn_d<64>(a, grid, s);
@@ -923,20 +986,34 @@ hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_
 
 // explicit instantiations: the host pass does not always emit launch stubs for kernel
 // templates that are only named inside hipLaunchKernelGGL
-template __global__ void k_attn<64, kPvFp8, false, false>(AttnArgs);
-template __global__ void k_attn<64, kPvFp8, true, false>(AttnArgs);
-template __global__ void k_attn<64, kPvFp8, false, true>(AttnArgs);
-template __global__ void k_attn<64, kPvFp8, true, true>(AttnArgs);
-template __global__ void k_attn<64, kPvBf16, false, false>(AttnArgs);
-template __global__ void k_attn<64, kPvBf16, true, false>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, false, false>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, true, false>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, false, true>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, true, true>(AttnArgs);
-template __global__ void k_attn<128, kPvBf16, false, false>(AttnArgs);
-template __global__ void k_attn<128, kPvBf16, true, false>(AttnArgs);
-template __global__ void k_attn_sparse<64>(AttnArgs);
-template __global__ void k_attn_sparse<128>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false, false, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false, false, true>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true, false, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true, false, true>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false, true, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, false, true, true>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true, true, false>(AttnArgs);
+template __global__ void k_attn<64, kPvFp8, true, true, true>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, false, false, false>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, false, false, true>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, true, false, false>(AttnArgs);
+template __global__ void k_attn<64, kPvBf16, true, false, true>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false, false, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false, false, true>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true, false, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true, false, true>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false, true, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, false, true, true>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true, true, false>(AttnArgs);
+template __global__ void k_attn<128, kPvFp8, true, true, true>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, false, false, false>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, false, false, true>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, true, false, false>(AttnArgs);
+template __global__ void k_attn<128, kPvBf16, true, false, true>(AttnArgs);
+template __global__ void k_attn_sparse<64, false>(AttnArgs);
+template __global__ void k_attn_sparse<64, true>(AttnArgs);
+template __global__ void k_attn_sparse<128, false>(AttnArgs);
+template __global__ void k_attn_sparse<128, true>(AttnArgs);
 template __global__ void k_debug_qk<64>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,
                                         int64_t, int, int, int, int32_t* __restrict__);
 template __global__ void k_debug_qk<128>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,

@@ -85,6 +85,8 @@ struct AttnArgs {
   const int32_t* tile_count = nullptr;
   const int32_t* tile_list = nullptr;
   int tiles_max = 0;
+  // compute units of the device: the period of the workgroup-pair issue priorities
+  int cu_count = 256;
 };
 
 // Operands of the block-sparse tile selection.
