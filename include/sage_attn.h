@@ -214,8 +214,9 @@ int sage_attn_fwd_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
  * B*H <= 65535 (else SAGE_EUNSUPPORTED); tau must be > 0 (else SAGE_EINVAL).
  *
  * sage_select_scratch_bytes - scratch size of sage_block_select.  After the call the
- *   scratch holds the code sums, int32 [2][B][H][Npad/64][d] (Q then K), and from the
- *   next 256-byte boundary the fp64 importance matrix [B][H][Npad/128][Npad/128].
+ *   scratch holds the code sums as two int8 digits, [2][B][H][Npad/64][2][d] (Q then K;
+ *   each sum s = 128 * digit0 + digit1, digit0 = s >> 7, digit1 = s & 127), and from
+ *   the next 256-byte boundary the fp64 importance matrix [B][H][Npad/128][Npad/128].
  * sage_block_select - the kept tiles from the quantised operands of sage_quant_qk
  *   (mode 0, device pointers, 256-byte aligned): tile_count [B][H][Npad/128] int32
  *   (k in every entry) and tile_list [B][H][Npad/128][Npad/128] int32, whose rows

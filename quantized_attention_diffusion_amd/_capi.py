@@ -328,7 +328,7 @@ def sage_block_select(quant: dict, density: float, return_importance: bool = Fal
         scratch.data_ptr(), scratch.numel(), _stream(dev)))
     if not return_importance:
         return count, lists
-    sums_bytes = -(-2 * B * H * (npad // 64) * d * 4 // 256) * 256
+    sums_bytes = -(-2 * B * H * (npad // 64) * 2 * d // 256) * 256     # code sums as two int8 digits
     imp = scratch[sums_bytes:sums_bytes + B * H * nt * nt * 8].view(torch.float64).reshape(B, H, nt, nt)
     return count, lists, imp
 

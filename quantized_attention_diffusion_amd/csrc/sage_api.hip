@@ -145,7 +145,7 @@ SelectLayout select_layout(int B, int H, int N, int d) {
   const int64_t npad = sage::padded_tokens(N);
   const size_t bh = (size_t)B * H;
   S.nt = (int)(npad / sage::kKvTile);
-  S.sums = 2 * bh * (npad / sage::kQuantBlock) * d * sizeof(int32_t);
+  S.sums = 2 * bh * (npad / sage::kQuantBlock) * 2 * d;   // two int8 digits per code sum
   S.imp = bh * S.nt * S.nt * sizeof(double);
   S.count = bh * S.nt * sizeof(int32_t);
   S.list = bh * S.nt * S.nt * sizeof(int32_t);
@@ -394,7 +394,7 @@ static int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v
     sa.q_i8 = qa.q_i8; sa.k_i8 = qa.k_i8; sa.q_scale = qa.q_scale; sa.k_scale = qa.k_scale;
     sa.B = B; sa.H = H; sa.N = N; sa.d = d; sa.npad = L.npad;
     sa.keep = keep_count(density, SL.nt);
-    sa.sums = (int32_t*)p;      p += round_up(SL.sums, kAlign);
+    sa.digits = (int8_t*)p;      p += round_up(SL.sums, kAlign);
     sa.imp = (double*)p;        p += round_up(SL.imp, kAlign);
     sa.tile_count = (int32_t*)p; p += round_up(SL.count, kAlign);
     sa.tile_list = (int32_t*)p;  p += round_up(SL.list, kAlign);
@@ -473,7 +473,7 @@ SAGE_EXPORT int sage_block_select(const int8_t* q_i8, const float* q_scale, cons
   sa.B = B; sa.H = H; sa.N = N; sa.d = d; sa.npad = L.npad;
   sa.keep = keep_count(density, SL.nt);
   char* p = (char*)scratch;
-  sa.sums = (int32_t*)p; p += round_up(SL.sums, kAlign);
+  sa.digits = (int8_t*)p; p += round_up(SL.sums, kAlign);
   sa.imp = (double*)p;
   sa.tile_count = tile_count;
   sa.tile_list = tile_list;

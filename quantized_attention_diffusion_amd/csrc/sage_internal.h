@@ -96,7 +96,8 @@ struct SelectArgs {
   int B, H, N, d;
   int64_t npad;
   int keep;                         // tiles kept per query block
-  int32_t* sums;                    // scratch [2][B*H][Npad/64][d]: per-block code sums of Q, K
+  int8_t* digits;                   // scratch [2][B*H][Npad/64][2][d]: per-block code sums of Q, K
+                                    // as int8 digits (sum = 128 * digit 0 + digit 1)
   double* imp;                      // scratch [B*H][Npad/128][Npad/128]: tile importance
   int32_t* tile_count;              // [B*H][Npad/128]
   int32_t* tile_list;               // [B*H][Npad/128][Npad/128]

@@ -161,9 +161,10 @@ def test_sparse_entry_points_validate(lib):
     B, H, N, d = 1, 24, 4608, 128
     nt = N // 128
     n = ctypes.c_size_t()
-    # scratch: Q and K code sums per 64-token block (int32) + the fp64 importance matrix
+    # scratch: Q and K code sums per 64-token block (two int8 digits per channel) + the
+    # fp64 importance matrix
     assert lib.sage_select_scratch_bytes(B, H, N, d, ctypes.byref(n)) == 0
-    assert n.value == 2 * B * H * (N // 64) * d * 4 + B * H * nt * nt * 8
+    assert n.value == 2 * B * H * (N // 64) * 2 * d + B * H * nt * nt * 8
     # the sparse workspace appends the scratch, tile_count and tile_list to the mode-0 one
     extra = _capi.sage_workspace_bytes_sparse(B, H, N, d) - _capi.sage_workspace_bytes(B, H, N, d)
     r256 = lambda x: -(-x // 256) * 256

@@ -131,6 +131,24 @@ def test_deterministic_runs():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
 
 
+def test_short_and_long_grids_agree():
+    # Grids of at most 4 x (compute units) workgroups launch the instance with
+    # workgroup-pair issue priorities, longer grids the plain one; the priorities only
+    # reorder instruction issue, so a head's output bits must not depend on the grid.
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    N, d = 1000, 128                                   # 8 query blocks per head
+    H = 4 * cus // 8 + 2
+    print(f"[grids] H={H} N={N}: {8 * H} workgroups against {8 * 2} for two heads", flush=True)
+    q, k, v = (t.cuda() for t in random_qkv(1, N, H, d, seed=25))
+    heads = slice(H - 2, H)
+    long_dense = sage.sage_attn_fwd(q, k, v)
+    short_dense = sage.sage_attn_fwd(q[:, :, heads], k[:, :, heads], v[:, :, heads])
+    assert torch.equal(long_dense[:, :, heads].contiguous().view(torch.int16), short_dense.view(torch.int16))
+    long_sparse = sage.sage_attn_fwd_sparse(q, k, v, 0.5)
+    short_sparse = sage.sage_attn_fwd_sparse(q[:, :, heads], k[:, :, heads], v[:, :, heads], 0.5)
+    assert torch.equal(long_sparse[:, :, heads].contiguous().view(torch.int16), short_sparse.view(torch.int16))
+
+
 def test_sm_scale_argument():
     q, k, v = random_qkv(1, 200, 2, 64, seed=24)
     out = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda(), sm_scale=0.05)
