@@ -113,6 +113,30 @@ def test_sparse_layouts_and_workspace_reuse():
     assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("kind", ["random", "equal_tiles", "zero_q"])
+@pytest.mark.parametrize("N,d,density", [(129 * 128, 64, 0.3), (200 * 128 - 77, 128, 0.05)],
+                         ids=["nt129", "nt200"])
+def test_selection_above_the_rank_limit(N, d, density, kind):
+    # more than 128 key tiles per head: the radix selection.  equal_tiles: every key
+    # tile holds the same keys, so each query block's importances tie and the lowest
+    # tiles must be kept; zero_q: all importances are signed zeros, equal in fp64.
+    print(f"[select radix] N={N} d={d} density={density} {kind}", flush=True)
+    q, k, v = random_qkv(1, N, 2, d, seed=31, outliers=0)
+    if kind == "equal_tiles":
+        reps = -(-N // 128)
+        k = k[:, :128].repeat(1, reps, 1, 1)[:, :N].contiguous()
+    elif kind == "zero_q":
+        q = torch.zeros_like(q)
+    gq = sage.sage_quant_qk(q.cuda(), k.cuda(), v.cuda())
+    cnt, lst, imp = sage.sage_block_select(gq, density, return_importance=True)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(_np(q), _np(k), _np(v))
+    _check_selection(cnt, lst, imp, ref, density, label=f"radix {kind}")
+    if kind == "zero_q" or (kind == "equal_tiles" and N % 128 == 0):   # a ragged last tile differs
+        keep = oracle.keep_count(density, -(-N // 128))
+        assert (lst[..., :keep].cpu() == torch.arange(keep, dtype=torch.int32)).all()
+
+
 @pytest.mark.parametrize("name,density,n_heads", [("flux_like", 0.3, 24), ("stress", 0.25, 2)])
 def test_full_size_sparse(name, density, n_heads):
     w = workloads.get(name)
