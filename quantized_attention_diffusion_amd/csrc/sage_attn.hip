@@ -11,7 +11,9 @@
 // P.V; TOK = one Q/K scale per token (the tile's key scales are staged in LDS with the
 // K tile); KBM = block-residual K (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 1:
 // the tile's two bf16 block means are staged with the K tile, and their products with
-// the query codes, on bf16 matrix cores, enter the logits).  The block-sparse kernel
+// the query codes, on bf16 matrix cores, enter the logits); PAIR = the issue priorities
+// that even out the two workgroups sharing a CU, chosen by the host for grids of at most
+// two rounds (IssuePriority).  The block-sparse kernel
 // (k_attn_sparse) is the FP8 body visiting only the key tiles its query block keeps
 // (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 4; the selection is in
 // sage_select.hip).

@@ -13,14 +13,14 @@
 // the integer dot products are exact in int64), so any implementation that follows
 // the formula takes the same decisions.  Ties go to the lower tile index.
 //
-// Three kernels: code sums per 64-token block (reads the INT8 operands once); the
-// importance matrix of each head (8 query blocks x 32 key tiles per workgroup, code
-// sums staged in LDS as int16 pairs for v_dot2_i32_i16); and the selection of each
-// query block: an MSB-first radix select of the k-th largest importance (as an
-// order-preserving 64-bit key), then the tiles above it and the first tiles equal to
-// it, compacted in ascending tile order with a workgroup prefix sum.  (Exact ranks,
-// one comparison of every tile against every other, and a bitonic sort in LDS
-// measured slower at 512 tiles.)
+// Three kernels: code sums per 64-token block (reads the INT8 operands once; each sum
+// stored as two int8 digits); the importance matrix of each head (32 query blocks x 32
+// key tiles per workgroup, the dot products of the digits on INT8 matrix cores); and
+// the selection of each query block, on order-preserving 64-bit keys of the
+// importances: exact ranks up to 128 tiles, above that an MSB-first radix select of
+// the k-th largest key, then the tiles above it and the first tiles equal to it; the
+// kept tiles are compacted in ascending order with a workgroup prefix sum.  (A bitonic
+// sort in LDS measured slower.)
 #include "sage_internal.h"
 
 namespace sage {
