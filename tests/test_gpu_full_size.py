@@ -44,7 +44,17 @@ def _head_quant(gq, h):
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_parity(name):
-    w = workloads.get(name)
+    _full_size_parity(workloads.get(name))
+
+
+def test_large_d64_two_batches_ragged():
+    # d = 64, B = 2 and a ragged last tile at a 16K-class length (the named workloads are
+    # all d = 128, B = 1)
+    _full_size_parity(workloads.Workload("d64_b2", B=2, H=8, N=16384 - 37, d=64, seed=5))
+
+
+def _full_size_parity(w):
+    name = w.name
     print(f"[full] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
     q, k, v = workloads.make_qkv(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
