@@ -53,6 +53,36 @@ def test_large_d64_two_batches_ragged():
     _full_size_parity(workloads.Workload("d64_b2", B=2, H=8, N=16384 - 37, d=64, seed=5))
 
 
+def test_offsets_beyond_int32():
+    # B*H*Npad*d = 3*100*65536*128 > 2^31 elements per tensor: heads past element 2^31 of
+    # every operand, the dense and the block-sparse step, checked on sampled rows of the
+    # first head and of the last heads
+    B, H, N, d = 3, 100, 65536, 128
+    assert B * H * N * d > 2 ** 31
+    print(f"[int64] B={B} H={H} N={N} d={d}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    q = torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = (torch.randn((B, N, H, d), generator=g, device="cuda")
+         + 3.0 * torch.randn((H, d), generator=g, device="cuda")).to(torch.bfloat16)
+    v = torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = sage.sage_attn_fwd(q, k, v)
+    sparse = sage.sage_attn_fwd_sparse(q, k, v, 0.25)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for b, h in [(0, 0), (B - 1, H - 1), (B - 1, H - 45)]:
+        print(f"    (b, h) = {(b, h)}: element offset {((b * H + h) * N * d) / 2 ** 31:.2f} x 2^31", flush=True)
+        qh, kh, vh = (t[b:b + 1, :, h:h + 1].float().cpu().numpy() for t in (q, k, v))
+        ref = oracle.quantize(qh, kh, vh)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=12, replace=False)]))
+        pipe = oracle.attention_pipeline(qh, kh, vh, rows=rows, quant=ref)
+        check_attention(to_np(out[b:b + 1, rows, h:h + 1, :]), pipe, f"int64 dense {(b, h)}")
+        _, tiles = oracle.select_tiles(ref, 0.25)
+        pipe_s = oracle.attention_pipeline(qh, kh, vh, rows=rows, quant=ref, tiles=tiles)
+        check_attention(to_np(sparse[b:b + 1, rows, h:h + 1, :]), pipe_s, f"int64 sparse {(b, h)}")
+    del q, k, v, out, sparse
+    torch.cuda.empty_cache()
+
+
 def _full_size_parity(w):
     name = w.name
     print(f"[full] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
