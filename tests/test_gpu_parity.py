@@ -171,6 +171,36 @@ def test_degenerate_inputs():
     assert torch.isfinite(out.float()).all()
 
 
+@pytest.mark.parametrize("kind", ["peaked", "huge_v", "tiny_qk", "outlier_key"])
+@pytest.mark.parametrize("pv", ["fp8", "bf16"])
+def test_extreme_magnitudes(kind, pv):
+    # peaked: logits of order 1e7 (base 2), every p but the row maximum's underflows to 0;
+    # huge_v: V times 2^13, which scales the V codes' scales and every later product by
+    # exactly 2^13, so the output must be 2^13 times the unscaled one, bit for bit (the
+    # absolute 2e-3 term of the bound is for V of order 1); tiny_qk: scales of order
+    # 1e-22 and logits that vanish against the exp2 offset (uniform attention);
+    # outlier_key: one key 1000x larger.
+    B, N, H, d = 1, 700, 2, 128
+    q, k, v = random_qkv(B, N, H, d, seed=26)
+    if kind == "peaked":
+        q, k = (q.float() * 300).to(torch.bfloat16), (k.float() * 300).to(torch.bfloat16)
+    elif kind == "huge_v":
+        base = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv=pv)
+        big = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), (v.float() * 8192).to(torch.bfloat16).cuda(), pv=pv)
+        assert torch.equal(big.float(), base.float() * 8192)
+        assert torch.isfinite(big.float()).all()
+    elif kind == "tiny_qk":
+        q, k = (q.float() * 1e-20).to(torch.bfloat16), (k.float() * 1e-20).to(torch.bfloat16)
+    else:
+        k[:, 333] = (k[:, 333].float() * 1000).to(torch.bfloat16)
+    print(f"[extreme] {kind} pv={pv}", flush=True)
+    out = sage.sage_attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), pv=pv)
+    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), kv_tile=KV_TILE, fp8_p=pv == "fp8",
+                                     fp8_v=pv == "fp8", bf16_p=pv == "bf16")
+    assert torch.isfinite(out.float()).all()
+    check_attention(to_np(out), pipe, f"extreme {kind} {pv}")
+
+
 def test_e4m3_conversion_matches_oracle_encoder():
     t = oracle.e4m3_table()[:0x7F]
     mids = (t[:-1] + t[1:]) / 2
