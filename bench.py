@@ -7,7 +7,7 @@ kernel's matrix-core roofline fraction, the quantisation pass's HBM rate, the sa
 figures at N=16384 and N=65536, and the CPU oracle timed on a bounded sample.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
-                [--no-cpu-baseline] [--pmc-run]
+                [--no-cpu-baseline] [--pmc-run] [--sparse-run WORKLOADS]
 """
 from __future__ import annotations
 
@@ -51,6 +51,10 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true",
                     help="only run the short program that the rocprofv3 counter runs profile")
+    ap.add_argument("--sparse-run", metavar="WORKLOADS", default=None,
+                    help="only run the block-sparse step a few times at each bench density on "
+                         "the comma-separated workloads (the program a rocprofv3 kernel trace "
+                         "of the tile selection profiles)")
     return ap.parse_args()
 
 
@@ -296,11 +300,33 @@ def pmc_run(w, reps: int = 3):
           file=sys.stderr, flush=True)
 
 
+def sparse_run(names: str):
+    """Block-sparse steps for a kernel trace: per workload and density of
+    SPARSE_DENSITIES, 5 steps (3 at 64K tokens and more) into a preallocated workspace."""
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    for name in names.split(","):
+        w = workloads.get(name)
+        q, k, v = (t.cuda() for t in workloads.make_qkv(w))
+        out = torch.empty_like(q)
+        ws = torch.empty(sage.sage_workspace_bytes_sparse(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+        for dens in SPARSE_DENSITIES:
+            for _ in range(5 if w.N < 60000 else 3):
+                sage.sage_attn_fwd_sparse(q, k, v, dens, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            print(f"[bench] sparse run {name} density {dens} done", file=sys.stderr, flush=True)
+        del q, k, v, out, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); heads would be "
-              "sharded across GPUs with no communication, see the design notes.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); across GPUs the "
+              "heads would be sharded, each GPU running this step on its share with no "
+              "communication.", file=sys.stderr)
         sys.exit(2)
     import workloads
 
@@ -308,7 +334,7 @@ def main():
     # The CPU baseline runs first, in worker processes started before this process
     # touches the GPU.
     cpu = None
-    if not args.no_cpu_baseline and not args.pmc_run:
+    if not args.no_cpu_baseline and not args.pmc_run and not args.sparse_run:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
         print(f"[bench] cpu baseline done: {cpu['sample']}", file=sys.stderr, flush=True)
@@ -322,6 +348,9 @@ def main():
         sys.exit(2)
     if args.pmc_run:
         pmc_run(w)
+        return
+    if args.sparse_run:
+        sparse_run(args.sparse_run)
         return
     # The longer sequences run first (they also bring the GPU to its working clocks);
     # the headline workload is timed last.

@@ -8,7 +8,7 @@ Sources (pages):
 * Quantising attention matrices from FP16 to INT8: bjdmk page
   "GitHub榜单静默期：Attention优化从架构转向推理加速", section 2.2.
 
-Readings of what the pages leave open (each also listed in the design notes):
+Readings of what the pages leave open:
 * K smoothing subtracts the per-(batch, head, channel) mean over the N valid tokens.
   The mean is summed in fp64, divided by N in fp64, rounded to fp32 and then to bf16
   (round to nearest even), and is stored in bf16.  K' = fp32(K) - fp32(mean), one fp32
