@@ -295,3 +295,155 @@ def test_block_mean_error_budget_matches_token_mean_on_synthetic_keys():
     r_tok = oracle.rel_l2(attention_pipeline(q, k, v, kv_tile=128), ex)
     r_blk = oracle.rel_l2(attention_pipeline(q, k, v, kv_tile=128, k_block_mean=True), ex)
     assert abs(r_blk - r_tok) < 0.003
+
+
+# ---- the plain (fp64) pipeline against definitions it must reduce to ----
+
+def _dequant_softmax(quant, v, b, h, sm):
+    """Textbook fp64 attention of the dequantised INT8 operands (natural exp, no base-2
+    logits, no tiles): q_deq = q_scale * q8, k_deq = k_scale * k8 (+ the block mean)."""
+    qb = quant["block"]
+    q8 = quant["q_i8"][b, h].astype(np.float64)
+    k8 = quant["k_i8"][b, h].astype(np.float64)
+    n = k8.shape[0]
+    qd = q8 * quant["q_scale"][b, h][np.arange(q8.shape[0]) // qb][:, None]
+    kd = k8 * quant["k_scale"][b, h][np.arange(n) // qb][:, None]
+    if "k_bmean" in quant:
+        kd = kd + quant["k_bmean"][b, h][np.arange(n) // 64].astype(np.float64)
+    s = (qd @ kd.T) * sm
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)) @ v[b, :, h, :].astype(np.float64)
+
+
+@pytest.mark.parametrize("mode", ["block64", "per_token", "block_mean"])
+def test_int8_pipeline_is_softmax_of_dequantised_operands(mode):
+    # FP8 rounding of P and V off: what is left is exact softmax of the dequantised
+    # Q and K, for any key tile.  A wrong scale index, a missing scale or a dropped
+    # block-mean term changes the logits and fails this.
+    q, k, v = _qkv(2, 300, 2, 64, seed=41, kbias=3.0)
+    k[:, :, :, 7] *= 20                                       # an outlier channel
+    quant = oracle.quantize(q, k, v, block=1 if mode == "per_token" else 64,
+                            k_block_mean=mode == "block_mean")
+    sm = oracle.default_sm_scale(64)
+    for T in (64, 128):
+        got64 = attention_pipeline(q, k, v, kv_tile=T, quant=quant, fp8_p=False, fp8_v=False)
+        got32 = attention_pipeline(q, k, v, kv_tile=T, quant=quant, fp8_p=False, fp8_v=False, arith="fp32")
+        for b in range(2):
+            for h in range(2):
+                want = _dequant_softmax(quant, v, b, h, sm)
+                assert np.abs(got64[b, :, h] - want).max() < 1e-12
+                assert np.abs(got32[b, :, h] - want).max() < 2e-5
+
+
+def test_online_single_tile_equals_two_pass_bitwise():
+    # T >= N: one tile, so the running maximum is the row maximum and the online
+    # recurrence must reduce to the two-pass form bit for bit, FP8 P and V included
+    q, k, v = _qkv(1, 200, 2, 64, seed=42, kbias=2.0)
+    quant = oracle.quantize(q, k, v)
+    sm = oracle.default_sm_scale(64)
+    got = attention_pipeline(q, k, v, kv_tile=256, quant=quant)
+    rows = np.arange(200)
+    for h in range(2):
+        s = oracle.pipeline_logits(q, k, quant, 0, h, rows, sm)
+        m = s.max(axis=1)
+        p = np.exp2(s - m[:, None])
+        l = p.sum(axis=1)
+        p8 = oracle.e4m3_decode(oracle.e4m3_encode(448.0 * p))
+        vv = oracle.e4m3_decode(quant["v_f8"][0, h])
+        two_pass = (p8 @ vv) / (448.0 * l[:, None]) * quant["v_scale"][0, h].astype(np.float64)[None, :]
+        assert np.array_equal(got[0, :, h], two_pass)
+
+
+@pytest.mark.parametrize("T", [32, 64, 128])
+def test_online_recurrence_equals_closed_form_over_tile_maxima(T):
+    # With FP8 P each code is rounded against the running maximum m_t after tile t.
+    # Unrolled, the recurrence is O = sum_t 2^(m_t - m_last) sum_{j in t}
+    # e4m3(448 * 2^(s_j - m_t)) v_j / (448 sum_j 2^(s_j - m_last)).
+    q, k, v = _qkv(1, 333, 2, 64, seed=43, kbias=2.0)
+    quant = oracle.quantize(q, k, v)
+    sm = oracle.default_sm_scale(64)
+    got = attention_pipeline(q, k, v, kv_tile=T, quant=quant)
+    rows = np.arange(333)
+    for h in range(2):
+        s = oracle.pipeline_logits(q, k, quant, 0, h, rows, sm)
+        vv = oracle.e4m3_decode(quant["v_f8"][0, h])
+        starts = list(range(0, 333, T))
+        mt = np.maximum.accumulate(np.stack([s[:, t0:t0 + T].max(axis=1) for t0 in starts]), axis=0)
+        m_last = mt[-1]
+        num = np.zeros((333, 64))
+        for t, t0 in enumerate(starts):
+            p8 = oracle.e4m3_decode(oracle.e4m3_encode(448.0 * np.exp2(s[:, t0:t0 + T] - mt[t][:, None])))
+            num += np.exp2(mt[t] - m_last)[:, None] * (p8 @ vv[t0:t0 + T])
+        den = 448.0 * np.exp2(s - m_last[:, None]).sum(axis=1)
+        want = num / den[:, None] * quant["v_scale"][0, h].astype(np.float64)[None, :]
+        assert np.abs(got[0, :, h] - want).max() < 1e-13
+
+
+def _two_key_case(delta_codes):
+    """One query, two keys whose base-2 logits differ by L * delta_codes (L = sm_scale *
+    log2 e with sm_scale 0.1), and one-hot V rows of 448 (v_scale 1/448), built
+    directly as quantised operands."""
+    d = 2
+    z = np.zeros((1, 2, 1, d), dtype=F32)
+    quant = dict(q_i8=np.array([[[[1, 0], [0, 0]]]], np.int8),
+                 q_scale=np.array([[[1.0]]], F32),
+                 k_i8=np.array([[[[0, 0], [-delta_codes, 0]]]], np.int8),
+                 k_scale=np.array([[[1.0]]], F32),
+                 k_mean=np.zeros((1, 1, d), F32),
+                 v_f8=np.array([[[[0x7E, 0], [0, 0x7E]]]], np.uint8),
+                 v_scale=np.full((1, 1, d), 1 / 448, F32), block=64)
+    return z, quant
+
+
+def test_p_codes_carry_the_static_scale_448():
+    # p0 = 1 and p1 = 2^(-0.1 * log2(e) * 3) = 0.7408: 448 * p1 = 331.9 rounds to the
+    # e4m3 value 320, while e4m3(p1) alone would be 0.75.  O = (p8 * v8 * v_scale) /
+    # (448 * l) with l = 1 + p1.
+    z, quant = _two_key_case(3)
+    p1 = 2.0 ** (-0.1 * oracle.LOG2E * 3)
+    assert oracle.e4m3_decode(oracle.e4m3_encode(448 * p1)) == 320.0
+    want = np.array([448.0, 320.0]) / (448.0 * (1 + p1))
+    for arith in ("fp64", "fp32"):
+        got = attention_pipeline(z, z, z, sm_scale=0.1, quant=quant, rows=[0], arith=arith)[0, 0, 0]
+        assert np.abs(got - want).max() < 1e-6, arith
+    # the same logits without the 448 would give 0.75 / (1 + p1) in channel 1
+    assert abs(0.75 / (1 + p1) - want[1]) > 0.02
+
+
+def test_fp32_reading_saturates_p_codes_at_huge_logits():
+    # With |logits| near 2^21 the fp32 roundings of the running maximum and of
+    # log2(448) - m leave up to ~1/4 in the exponent either way, so the row maximum's
+    # p lies anywhere in about [377, 608]; above 464 an unsaturated e4m3 conversion
+    # gives NaN.  The reading saturates the code at 448 while l keeps the unrounded p,
+    # so every output row is a finite positive multiple of one dequantised V row, and
+    # the rows whose p passed 464 have a factor below 448/464.
+    q, k, v = _qkv(1, 256, 1, 128, seed=44)
+    q, k = q * 1000, k * 1000
+    quant = oracle.quantize(q, k, v)
+    o = attention_pipeline(q, k, v, quant=quant, arith="fp32")[0, :, 0]
+    assert np.isfinite(o).all()
+    vd = oracle.e4m3_decode(quant["v_f8"][0, 0]) * quant["v_scale"][0, 0].astype(np.float64)[None, :]
+    s = oracle.pipeline_logits(q, k, quant, 0, 0, np.arange(256), oracle.default_sm_scale(128))
+    jmax = s.argmax(axis=1)
+    ratio = (o * vd[jmax]).sum(axis=1) / (vd[jmax] ** 2).sum(axis=1)
+    assert np.abs(o - ratio[:, None] * vd[jmax]).max() < 1e-9
+    assert (ratio > 448 / 620).all() and (ratio < 1.1).all() and (ratio < 448 / 464).sum() >= 10
+    # the plain reading keeps p = 1 at the maximum: exactly the V row
+    o64 = attention_pipeline(q, k, v, quant=quant)[0, :, 0]
+    assert np.abs(o64 - vd[jmax]).max() < 1e-12
+
+
+def test_fp32_and_fp64_readings_agree_on_the_workloads():
+    # the two readings differ only where an fp32 rounding moves a P code across an
+    # e4m3 rounding boundary: within 1e-4 on the tiny workload and on sampled rows of
+    # one head of the Flux-like and stress shapes
+    cases = [(workloads.get("tiny"), None),
+             (workloads.Workload("flux_head", B=1, H=1, N=4608, d=128), 48),
+             (workloads.Workload("stress_head", B=1, H=1, N=65536, d=128, outliers=4), 12)]
+    for w, nrows in cases:
+        q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+        quant = oracle.quantize(q, k, v)
+        rows = None if nrows is None else np.random.default_rng(0).choice(w.N, nrows, replace=False)
+        a = attention_pipeline(q, k, v, quant=quant, rows=rows)
+        b = attention_pipeline(q, k, v, quant=quant, rows=rows, arith="fp32")
+        assert np.abs(a - b).max() < 1e-4, w.name
