@@ -136,16 +136,24 @@ int sage_quant_qk_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      void* scratch, size_t scratch_bytes, void* stream);
 
 /*
- * sage_attn_fwd_prequant - fused attention on quantised operands.
+ * sage_attn_fwd_prequant - fused attention on quantised operands (mode 0 layouts).
+ * Sources: Q.K^T on INT8 and P.V on FP8 (juejin page "MiniMax H3 接入 SageAttention
+ * 实测加速", section 一); the result is softmax(Q K^T * sm_scale) V (Baidu Cloud page
+ * "SDPA稠密注意力模式", section 三 part 1), computed block by block, the score matrix
+ * never written out (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速",
+ * section 2.2).
  * For each query i, keys are visited in tiles of kv_tile (sage_kernel_info) keys:
  *   S = q_i8 . k_i8^T exactly in int32 (INT8 matrix cores),
  *   base-2 logits s = S * fp32(fp32(q_scale*fp32(sm_scale*log2 e)) * k_scale),
  *   fp32 online softmax with exp2 (running max m, p = 448 * 2^(s - m)),
- *   P rounded to e4m3, acc += P8 . V8 (FP8 matrix cores, fp32 accumulation),
- *   l accumulates the unrounded p; O = acc * v_scale / l, written as bf16 (RNE)
- *   through the [B][H][N][d] view `out` (strides so).
+ *   P rounded to e4m3 (nearest even, saturating at 448), acc += P8 . V8 (FP8 matrix
+ *   cores, fp32 accumulation), l accumulates the unrounded p; O = acc * v_scale / l,
+ *   written as bf16 (RNE) through the [B][H][N][d] view `out` (strides so).
  * Keys and queries at index >= N are never read as data: keys are masked, rows
- * beyond N are not written.  sm_scale must be finite and > 0.
+ * beyond N are not written.  sm_scale: 0 selects 1/sqrt(d) (rounded once to fp32);
+ * otherwise it must be finite and > 0 (else SAGE_EINVAL).
+ * Buffers: the quantised operands (device, 256-byte aligned, owned by the caller,
+ * read only); `out` must not overlap them.
  */
 int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale,
@@ -154,11 +162,16 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
                            int B, int H, int N, int d, float sm_scale, void* stream);
 
 /*
- * sage_attn_fwd - the whole hot path: sage_quant_qk into the workspace, then
- * sage_attn_fwd_prequant.  strides[0..3] describe q, k, v and out.
- * workspace: >= sage_workspace_bytes() bytes, 256-byte aligned.  After the call
- * the workspace holds the quantised operands in this order, each region starting
- * on a 256-byte boundary: q_i8, k_i8, v_f8, q_scale, k_scale, k_mean, v_scale.
+ * sage_attn_fwd - the whole hot path, O = softmax(Q K^T * sm_scale) V (Baidu Cloud page
+ * "SDPA稠密注意力模式", section 三 part 1) by the quantised method: K smoothing, INT8
+ * Q.K^T and FP8 P.V (juejin page "MiniMax H3 接入 SageAttention 实测加速", section 一),
+ * i.e. sage_quant_qk into the workspace, then sage_attn_fwd_prequant on it.
+ * q, k, v, out: bf16 device views; strides[0..3] describe q, k, v and out; out must
+ * not overlap q, k, v or the workspace.  sm_scale as for sage_attn_fwd_prequant.
+ * workspace: >= sage_workspace_bytes() bytes, 256-byte aligned, owned by the caller.
+ * After the call the workspace holds the quantised operands in this order, each
+ * region starting on a 256-byte boundary: q_i8, k_i8, v_f8, q_scale, k_scale, k_mean,
+ * v_scale.
  */
 int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                   int B, int H, int N, int d, float sm_scale,

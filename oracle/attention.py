@@ -175,19 +175,22 @@ def bf16_round64(x) -> np.ndarray:
     return np.copysign(np.where(a == 0, 0.0, r), x)
 
 
-def pipeline_logits(q, k, quant, b, h, rows, sm_scale, int8_qk=True) -> np.ndarray:
+def pipeline_logits(q, k, quant, b, h, rows, sm_scale, int8_qk=True, with_mean_term=False):
     """fp64 base-2 logits of the dequantised operands for query tokens ``rows`` of head
     (b, h) against every key: sm_scale * log2(e) * q_deq . k_deq^T.  With INT8 operands
     q_deq = q_scale * q8 and k_deq = k_scale * k8 (+ the block mean with block-residual
     K; the token mean of plain smoothing drops out of the softmax), so
         s = sm_scale * log2(e) * q_scale_i * (k_scale_j * S_ij [+ q8_i . mu_b(j)]).
-    Without INT8 (``int8_qk=False``) the bf16 inputs themselves.  Returns [R, Nk]."""
+    Without INT8 (``int8_qk=False``) the bf16 inputs themselves.  Returns [R, Nk]; with
+    ``with_mean_term`` also the block-mean part sm_scale * log2(e) * q_scale_i * q8_i .
+    mu_b(j) of each logit (zeros without block-residual K)."""
     L = float(sm_scale) * LOG2E
     r = np.asarray(rows, dtype=np.int64)
     if not int8_qk:
         qh = np.asarray(q, dtype=np.float64)[b, r, h, :]
         kh = np.asarray(k, dtype=np.float64)[b, :, h, :]
-        return L * (qh @ kh.T)
+        s = L * (qh @ kh.T)
+        return (s, np.zeros_like(s)) if with_mean_term else s
     qb = int(quant.get("block", QUANT_BLOCK))
     q8 = quant["q_i8"][b, h][r]                                     # [R, d]
     k8 = quant["k_i8"][b, h]                                        # [Nk, d]
@@ -196,10 +199,15 @@ def pipeline_logits(q, k, quant, b, h, rows, sm_scale, int8_qk=True) -> np.ndarr
     ks = quant["k_scale"][b, h][np.arange(nk) // qb].astype(np.float64)
     t = ks[None, :] * qk_int32(q8, k8).astype(np.float64)           # k_scale * S
     kbm = quant.get("k_bmean")
+    Dk = None
     if kbm is not None:
         D = q8.astype(np.float64) @ kbm[b, h].astype(np.float64).T  # exact, [R, nblk]
-        t = t + D[:, np.arange(nk) // QUANT_BLOCK]
-    return (L * qs)[:, None] * t
+        Dk = D[:, np.arange(nk) // QUANT_BLOCK]
+        t = t + Dk
+    s = (L * qs)[:, None] * t
+    if not with_mean_term:
+        return s
+    return s, ((L * qs)[:, None] * Dk if Dk is not None else np.zeros_like(s))
 
 
 def _round_p(x, fp8_p: bool, bf16_p: bool) -> np.ndarray:
@@ -214,7 +222,8 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                        quant=None, int8_qk: bool = True, fp8_p: bool = True,
                        fp8_v: bool = True, smooth_k: bool = True,
                        bf16_p: bool = False, block: int = QUANT_BLOCK,
-                       k_block_mean: bool = False, tiles=None, arith: str = "fp64") -> np.ndarray:
+                       k_block_mean: bool = False, tiles=None, arith: str = "fp64",
+                       code_margin: bool = False):
     """Quantised attention.  q, k, v: float32 [B, N, H, d] holding bf16 values.
 
     ``quant``: the dict of :func:`oracle.quantize` if already computed.  ``rows``:
@@ -230,12 +239,17 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     I*kv_tile ...) visits.  None visits every tile.
     ``arith``: "fp64" (the plain reading, default) or "fp32" (P codes decided in fp32;
     module docstring).
+    ``code_margin`` (fp64 only): also return, per output, how far it can move when every
+    P code that an fp32 evaluation may round the other way takes its other value (see
+    ``_online_fp64``).
     The keys are those of ``quant`` (their count may differ from the queries').
-    Returns fp64 [B, R, H, d]."""
+    Returns fp64 [B, R, H, d] (with ``code_margin``: that array and the margins)."""
     if fp8_p and bf16_p:
         raise ValueError("P is rounded either to e4m3 or to bf16, not both")
     if arith not in ("fp64", "fp32"):
         raise ValueError("arith is 'fp64' or 'fp32'")
+    if code_margin and arith != "fp64":
+        raise ValueError("code_margin belongs to the fp64 reading")
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     v = np.asarray(v, dtype=F32)
@@ -246,6 +260,7 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
     r = _rows(N, rows)
     Nk = int(quant["k_i8"].shape[2]) if int8_qk else k.shape[1]
     out = np.empty((B, len(r), H, d), dtype=np.float64)
+    margin = np.zeros_like(out) if code_margin else None
     T = int(kv_tile)
     for b in range(B):
         for h in range(H):
@@ -265,22 +280,43 @@ def attention_pipeline(q, k, v, sm_scale=None, kv_tile: int = 128, rows=None,
                 starts = (range(0, Nk, T) if tiles is None
                           else [int(J) * T for J in tiles[b][h][int(rr[0]) // T]])
                 if arith == "fp64":
-                    o = _online_fp64(pipeline_logits(q, k, quant, b, h, rr, sm, int8_qk),
-                                     vv, starts, T, Nk, fp8_p, bf16_p)
+                    s_all, e_all = pipeline_logits(q, k, quant, b, h, rr, sm, int8_qk, with_mean_term=True)
+                    o, amb = _online_fp64(s_all, vv, starts, T, Nk, fp8_p, bf16_p,
+                                          e_all if code_margin else None)
+                    if code_margin:
+                        margin[b, pos, h, :] = amb * np.abs(vs)[None, :]
                 else:
                     o = _online_fp32(q, k, quant, b, h, rr, sm, int8_qk, vv, starts, T, Nk,
                                      fp8_p, bf16_p)
                 out[b, pos, h, :] = o * vs[None, :]
-    return out
+    return (out, margin) if code_margin else out
 
 
-def _online_fp64(s_all, vv, starts, T, Nk, fp8_p, bf16_p):
+# Bound on the difference between an fp32 evaluation of a P code's exponent argument
+# (the ``arith="fp32"`` order, or an implementation of it) and the exact s - m + log2(448):
+# every fp32 operation on the way (the scale products, the logit, the block-mean term,
+# the maximum, log2(448) - m, the fused multiply-add, exp2 to within two ulps) adds at
+# most a few units of 2^-24 times the magnitudes involved; summed, they stay below
+# 2^-19 * (|s| + |e| + |m| + 1.5), e the block-mean part of the logit.
+FP32_ARG_ERR = 2.0 ** -19
+
+
+def _online_fp64(s_all, vv, starts, T, Nk, fp8_p, bf16_p, e_all=None):
     """The online softmax of the plain reading over the key tiles beginning at
-    ``starts``; returns acc / (448 l) (V scales not applied)."""
+    ``starts``; returns (acc / (448 l), margin) with the V scales not applied.
+
+    margin (computed when ``e_all``, the block-mean part of the logits, is given): a P
+    code is ambiguous when 448 p lies within the relative bound E = FP32_ARG_ERR * (|s| +
+    |e| + |m| + 1.5) of a rounding boundary of its format, i.e. when an fp32 evaluation
+    may take the neighbouring code; margin sums, through the same online rescaling,
+    |code(448 p (1 + E)) - code(448 p (1 - E))| * |v8| / (448 l): how far the output
+    can move if every ambiguous code flips."""
     R = s_all.shape[0]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     acc = np.zeros((R, vv.shape[1]))
+    amb = np.zeros_like(acc) if e_all is not None else None
+    rounds = fp8_p or bf16_p
     for t0 in starts:
         t1 = min(Nk, t0 + T)
         s = s_all[:, t0:t1]
@@ -289,8 +325,16 @@ def _online_fp64(s_all, vv, starts, T, Nk, fp8_p, bf16_p):
         p = np.exp2(s - m_new[:, None])
         l = alpha * l + p.sum(axis=1)
         acc = alpha[:, None] * acc + _round_p(P_SCALE * p, fp8_p, bf16_p) @ vv[t0:t1]
+        if amb is not None:
+            amb = alpha[:, None] * amb
+            if rounds:
+                E = FP32_ARG_ERR * (np.abs(s) + np.abs(e_all[:, t0:t1]) + np.abs(m_new)[:, None] + 1.5)
+                x = P_SCALE * p
+                flip = _round_p(x * (1 + E), fp8_p, bf16_p) - _round_p(x * (1 - E), fp8_p, bf16_p)
+                amb = amb + flip @ np.abs(vv[t0:t1])
         m = m_new
-    return acc / (P_SCALE * l[:, None])
+    o = acc / (P_SCALE * l[:, None])
+    return o, (amb / (P_SCALE * l[:, None]) if amb is not None else None)
 
 
 def _online_fp32(q, k, quant, b, h, rr, sm, int8_qk, vv, starts, T, Nk, fp8_p, bf16_p):

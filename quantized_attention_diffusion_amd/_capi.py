@@ -175,20 +175,37 @@ def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _alloc_quant(B, H, N, d, dev, mode=0):
+def _quant_specs(B, H, N, d, mode=0) -> dict:
+    """(shape, dtype) of every quantised operand of sage_quant_qk_ex in ``mode``."""
     npad = sage_padded_tokens(N)
     nsc = npad if mode & SAGE_QK_PER_TOKEN else npad // 64
     vdt = torch.bfloat16 if mode & SAGE_PV_BF16 else torch.uint8
     return dict(
-        q_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
-        q_scale=torch.empty((B, H, nsc), dtype=torch.float32, device=dev),
-        k_i8=torch.empty((B, H, npad, d), dtype=torch.int8, device=dev),
-        k_scale=torch.empty((B, H, nsc), dtype=torch.float32, device=dev),
-        k_mean=torch.empty((B, H, npad // 64, d) if mode & SAGE_K_BLOCK_MEAN else (B, H, d),
-                           dtype=torch.bfloat16, device=dev),
-        v_f8=torch.empty((B, H, d, npad), dtype=vdt, device=dev),
-        v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+        q_i8=((B, H, npad, d), torch.int8),
+        q_scale=((B, H, nsc), torch.float32),
+        k_i8=((B, H, npad, d), torch.int8),
+        k_scale=((B, H, nsc), torch.float32),
+        k_mean=((B, H, npad // 64, d) if mode & SAGE_K_BLOCK_MEAN else (B, H, d), torch.bfloat16),
+        v_f8=((B, H, d, npad), vdt),
+        v_scale=((B, H, d), torch.float32),
     )
+
+
+def _alloc_quant(B, H, N, d, dev, mode=0):
+    return {name: torch.empty(shape, dtype=dt, device=dev)
+            for name, (shape, dt) in _quant_specs(B, H, N, d, mode).items()}
+
+
+def _check_quant_out(o: dict, B, H, N, d, dev, mode):
+    """A caller-supplied operand dict must match the layout of ``mode`` exactly: the
+    library writes that many bytes into each buffer."""
+    for name, (shape, dt) in _quant_specs(B, H, N, d, mode).items():
+        t = o.get(name)
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"out[{name!r}] is missing")
+        if t.dtype != dt or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"out[{name!r}] must be a contiguous {dt} tensor of shape {tuple(shape)} on "
+                             f"{dev} for mode {mode} (got {t.dtype} {tuple(t.shape)} on {t.device})")
 
 
 def sage_quant_qk(q, k, v, layout: str = "bnhd", out: dict | None = None,
@@ -210,6 +227,8 @@ def sage_quant_qk_ex(q, k, v, mode: int, layout: str = "bnhd", out: dict | None 
     if dk != (B, H, N, d) or dv != (B, H, N, d):
         raise ValueError("q, k and v must have the same shape")
     dev = q.device
+    if out is not None:
+        _check_quant_out(out, B, H, N, d, dev, mode)
     o = out if out is not None else _alloc_quant(B, H, N, d, dev, mode)
     if scratch is None:
         scratch = torch.empty(sage_quant_scratch_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
@@ -227,13 +246,18 @@ def sage_quant_qk_ex(q, k, v, mode: int, layout: str = "bnhd", out: dict | None 
     return o
 
 
-def _default_scale(d: int) -> float:
-    return float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+def _scale_arg(sm_scale) -> float:
+    """None selects the library's default 1/sqrt(d) (passed as 0)."""
+    return 0.0 if sm_scale is None else float(sm_scale)
 
 
 def sage_attn_fwd_prequant(quant: dict, out: torch.Tensor | None = None,
                            sm_scale: float | None = None, layout: str = "bnhd") -> torch.Tensor:
-    """Attention on operands produced by :func:`sage_quant_qk`.  Returns ``out``."""
+    """Attention on operands produced by :func:`sage_quant_qk` (mode 0: the C entry
+    point takes 64-token scales and FP8 V only).  Returns ``out``."""
+    if int(quant.get("mode", 0)) != 0:
+        raise ValueError(f"sage_attn_fwd_prequant takes mode-0 operands (got mode {quant['mode']}); "
+                         "use sage_attn_fwd_ex for the other modes")
     B, H, npad, d = quant["q_i8"].shape
     N = int(quant["N"])
     dev = quant["q_i8"].device
@@ -244,7 +268,7 @@ def sage_attn_fwd_prequant(quant: dict, out: torch.Tensor | None = None,
     dims, so = _dims(out, layout)
     if dims != (B, H, N, d):
         raise ValueError(f"out has dims {dims}, expected {(B, H, N, d)}")
-    sm = _default_scale(d) if sm_scale is None else float(sm_scale)
+    sm = _scale_arg(sm_scale)
     _check(load().sage_attn_fwd_prequant(
         quant["q_i8"].data_ptr(), quant["q_scale"].data_ptr(), quant["k_i8"].data_ptr(),
         quant["k_scale"].data_ptr(), quant["v_f8"].data_ptr(), quant["v_scale"].data_ptr(),
@@ -285,7 +309,7 @@ def sage_attn_fwd_ex(q, k, v, out: torch.Tensor | None = None, sm_scale: float |
         raise ValueError("out must have the shape of q")
     if workspace is None:
         workspace = torch.empty(sage_workspace_bytes_ex(B, H, N, d, mode), dtype=torch.uint8, device=dev)
-    sm = _default_scale(d) if sm_scale is None else float(sm_scale)
+    sm = _scale_arg(sm_scale)
     strides = (sage_strides * 4)(sq, sk, sv, so)
     if _entry == "sage_attn_fwd":
         _check(load().sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -354,7 +378,7 @@ def sage_attn_fwd_sparse(q, k, v, density: float, out: torch.Tensor | None = Non
         raise ValueError("out must have the shape of q")
     if workspace is None:
         workspace = torch.empty(sage_workspace_bytes_sparse(B, H, N, d), dtype=torch.uint8, device=dev)
-    sm = _default_scale(d) if sm_scale is None else float(sm_scale)
+    sm = _scale_arg(sm_scale)
     strides = (sage_strides * 4)(sq, sk, sv, so)
     _check(load().sage_attn_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                        B, H, N, d, sm, strides, float(density), _stream(dev),

@@ -178,6 +178,18 @@ int launch_status(hipError_t e, const char* what) {
 }
 
 float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
+
+// sm_scale 0 selects the definition's 1/sqrt(d) (rounded once to fp32); anything else
+// must be finite and positive.
+int resolve_sm_scale(float& sm_scale, int d) {
+  if (sm_scale == 0.0f) {
+    sm_scale = (float)(1.0 / sqrt((double)d));
+    return SAGE_OK;
+  }
+  if (!(sm_scale > 0.0f) || !isfinite(sm_scale))
+    return fail(SAGE_EINVAL, "sm_scale must be 0 (default 1/sqrt(d)) or finite and > 0 (got %g)", (double)sm_scale);
+  return SAGE_OK;
+}
 float log2_pscale() { return (float)log2(448.0); }
 
 }  // namespace
@@ -311,8 +323,7 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
   for (int i = 0; i < 6; ++i)
     if (overlaps(eo, Extent{(uintptr_t)ins[i], (uintptr_t)ins[i] + sizes[i]}))
       return fail(SAGE_EINVAL, "out overlaps %s", names[i]);
-  if (!(sm_scale > 0.0f) || !isfinite(sm_scale))
-    return fail(SAGE_EINVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (int rc = resolve_sm_scale(sm_scale, d)) return rc;
 
   sage::AttnArgs a;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale;
@@ -345,8 +356,7 @@ static int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v
   for (int i = 0; i < 3; ++i)
     if (overlaps(eo, extent(ins[i], strides[i], B, H, N, d)))
       return fail(SAGE_EINVAL, "out overlaps %s", names[i]);
-  if (!(sm_scale > 0.0f) || !isfinite(sm_scale))
-    return fail(SAGE_EINVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (int rc = resolve_sm_scale(sm_scale, d)) return rc;
   const QuantLayout L = layout(B, H, N, d, mode);
   const SelectLayout SL = select_layout(B, H, N, d);
   const size_t need = workspace_size(L) +

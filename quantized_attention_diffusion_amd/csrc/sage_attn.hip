@@ -50,6 +50,7 @@
 #include <atomic>
 #include "sage_internal.h"
 #include "sage_device.h"
+#include "sage_tiles.h"
 
 namespace sage {
 
@@ -57,55 +58,18 @@ constexpr int G = kGroupsPerWave;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// LDS tiles are unpadded and XOR-swizzled at 16-byte granularity so that the 128-bit
-// operand reads below run without bank conflicts:
-//   K tile [128 keys][D bytes]:    physical chunk = chunk ^ kswz(key)
-//   V tile [D channels][128 keys]: physical chunk = chunk ^ vswz(channel)
-// A K read touches keys 32*(r/4) + 4*kt + r%4 (r = lane % 16), i.e. varies key bits
-// 0, 1, 5, 6 across the wave; a V read touches channels 16*dt + r.  The K swizzle is a
-// linear map of those four key bits onto the three chunk bits; gfx950's bank grouping
-// for 128-bit reads is not documented, so it was chosen by timing all 4096 such maps on
-// the exact K read pattern (about a third run at the conflict-free rate; the obvious
-// maps for 16- or 32-lane passes do not).  The V swizzle runs at the contiguous rate.
-template <int D>
-__device__ __forceinline__ int kswz(int key) {
-  if constexpr (D == 128)
-    return ((key ^ (key >> 1) ^ (key >> 6)) & 1) | (((key ^ (key >> 5)) & 1) << 1) | (((key >> 6) & 1) << 2);
-  else
-    return (key >> 5) & 3;
-}
-__device__ __forceinline__ int vswz(int ch) { return ((ch ^ (ch >> 3)) & 1) | (ch & 6); }
-// bf16 V tile [D channels][128 keys], 256 bytes per channel: physical chunk = chunk ^
-// v16swz(channel).  A read touches channels 16*dt + r and chunks 4g + s; the map is
-// linear in channel bits 0-3 and was chosen by timing all 2^16 such maps on this
-// pattern (about 30% run at the conflict-free rate, the plain XOR with the channel at
-// half of it).
-__device__ __forceinline__ int v16swz(int ch) {
-  const int b0 = ch & 1, b1 = (ch >> 1) & 1, b2 = (ch >> 2) & 1, b3 = (ch >> 3) & 1;
-  return b1 | ((b1 ^ b2 ^ b3) << 1) | ((b1 ^ b3) << 2) | ((b0 ^ b1 ^ b2 ^ b3) << 3);
-}
-
-template <int D>
-struct Lds {
-  static constexpr int KBYTES = kKvTile * D;       // one K tile
-  static constexpr int VBYTES = D * kKvTile;       // one e4m3 V tile
-  static constexpr int V16BYTES = D * kKvTile * 2; // one bf16 V tile
-};
-
-// Per-lane LDS byte offsets of the matrix-core operand reads.  The swizzles depend only
-// on key bits 0, 1, 5, 6 and channel bits 0-3, so the offset of K sub-tile kt is
-// koff[kk] + kt * 4 * D and that of V channel tile dt is voff[half] + dt * 16 * 128.
+// Per-lane LDS byte offsets of the matrix-core operand reads (sage_tiles.h): the
+// offset of K sub-tile kt is koff[kk] + kt * 4 * D and that of V channel tile dt is
+// voff[half] + dt * 16 * 128.
 template <int D>
 struct LaneOffsets {
   int koff[D / 64];
   int voff[2];
   __device__ __forceinline__ explicit LaneOffsets(int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    const int key = 32 * (r >> 2) + (r & 3);
 #pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) koff[kk] = key * D + 16 * ((4 * kk + g) ^ kswz<D>(key));
+    for (int kk = 0; kk < D / 64; ++kk) koff[kk] = k_read_offset<D>(lane, kk);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) voff[h] = r * kKvTile + 16 * ((2 * g + h) ^ vswz(r));
+    for (int h = 0; h < 2; ++h) voff[h] = v_read_offset(lane, h);
   }
 };
 
@@ -114,31 +78,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Per-lane source offsets of the LDS DMA copies (computed once per kernel): the K tile
-// copy of wave w, instruction j reads K + koff[j], the V tile copy V + voff[j] (bytes,
-// relative to the tile's first key), which lands at LDS offset (w*PW + j)*1024 + 16*lane:
-// buffer_load_dwordx4 ... lds writes lane i's 16 bytes at 16*i of the instruction's 1 KB, so
-// the swizzle is applied by choosing which global chunk lane i reads.
+// Per-lane source offsets of the LDS DMA copies (computed once per kernel, sage_tiles.h):
+// the K tile copy of wave w, instruction j reads K + koff[j], the V tile copy V + voff[j]
+// (bytes, relative to the tile's first key), which lands at LDS offset
+// dma_lds_offset(w, j, PW, lane).
 template <int D>
 struct DmaOffsets {
-  static constexpr int KPW = Lds<D>::KBYTES / 1024 / kWaves;
-  static constexpr int VPW = Lds<D>::VBYTES / 1024 / kWaves;
+  static constexpr int KPW = DmaShape<D>::KPW;
+  static constexpr int VPW = DmaShape<D>::VPW;
   static constexpr int PER_TILE = KPW + VPW;     // DMA instructions per wave per tile
   uint32_t koff[KPW];
   uint32_t voff[VPW];
   __device__ __forceinline__ DmaOffsets(int wave, int lane, int64_t npad) {
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int pos = (wave * KPW + j) * 1024 + lane * 16;
-      const int key = pos / D, pc = (pos % D) / 16;
-      koff[j] = (uint32_t)(key * D + (pc ^ kswz<D>(key)) * 16);
-    }
+    for (int j = 0; j < KPW; ++j) koff[j] = k_dma_src<D>(wave, j, lane);
 #pragma unroll
-    for (int j = 0; j < VPW; ++j) {
-      const int pos = (wave * VPW + j) * 1024 + lane * 16;
-      const int ch = pos / kKvTile, pc = (pos % kKvTile) / 16;
-      voff[j] = (uint32_t)(ch * npad + (pc ^ vswz(ch)) * 16);
-    }
+    for (int j = 0; j < VPW; ++j) voff[j] = v_dma_src<D>(wave, j, lane, npad);
   }
   // tile_off: byte offset of the tile inside the buffer (a scalar operand)
   __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t kbufr, int tile_off, uint8_t* klds, int wave) const {
@@ -161,23 +116,18 @@ template <int D>
 struct LaneOffsets16 {
   int voff[4];
   __device__ __forceinline__ explicit LaneOffsets16(int lane) {
-    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) voff[s] = r * 256 + 16 * ((4 * g + s) ^ v16swz(r));
+    for (int s = 0; s < 4; ++s) voff[s] = v16_read_offset(lane, s);
   }
 };
 
 template <int D>
 struct DmaOffsets16 {
-  static constexpr int VPW = Lds<D>::V16BYTES / 1024 / kWaves;
+  static constexpr int VPW = DmaShape<D>::V16PW;
   uint32_t voff[VPW];
   __device__ __forceinline__ DmaOffsets16(int wave, int lane, int64_t npad) {
 #pragma unroll
-    for (int j = 0; j < VPW; ++j) {
-      const int pos = (wave * VPW + j) * 1024 + lane * 16;
-      const int ch = pos / 256, pc = (pos % 256) / 16;
-      voff[j] = (uint32_t)(ch * npad * 2 + (pc ^ v16swz(ch & 15)) * 16);
-    }
+    for (int j = 0; j < VPW; ++j) voff[j] = v16_dma_src<D>(wave, j, lane, npad);
   }
   __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t vbufr, int tile_off, uint8_t* vlds, int wave) const {
 #pragma unroll
@@ -255,6 +205,42 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 // Two fp32 values -> two bf16 (round to nearest even), first value in the low half.
 __device__ __forceinline__ int pk_bf16(float a, float b) {
   return __builtin_bit_cast(int, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
+// Saturation of the FP8 P codes.  p = 448 * 2^(s - m) is at most 448 up to the fp32
+// roundings of the running maximum m, of log2(448) - m and (block-residual K) of the
+// block-mean term e, each at most half an ulp of a value below 2^17 when |m| and |e|
+// stay below 2^16: together less than 2^-5 in the exponent, so p < 448 * 2^(2^-5) <
+// 464, which v_cvt_pk_fp8_f32 rounds to 448 (it gives the NaN code 0x7F from 464 up).
+// Tiles whose |m| or |e| reach 2^16 (base-2 logits of 65536: only for inputs far
+// outside attention's usual range) replace every 0x7F code of P by 0x7E (448) after
+// the conversion, as an e4m3 encoder that saturates does; l sums the unclamped p.
+constexpr float kSatLimit = 65536.0f;
+
+// Four e4m3 codes of non-negative values (bytes 0x00 .. 0x7F): 0x7F -> 0x7E.  A byte
+// is 0x7F exactly when adding 1 sets its top bit, with no carry into the next byte.
+__device__ __forceinline__ int e4m3x4_saturate(int w) {
+  const uint32_t u = (uint32_t)w;
+  return (int)(u - (((u + 0x01010101u) & 0x80808080u) >> 7));
+}
+
+__device__ __forceinline__ bool wave_any(bool c) { return __ballot(c) != 0ull; }
+
+template <bool BM>
+__device__ __forceinline__ bool saturate_tile(const float (&m)[kGroupsPerWave], const float (&e)[kGroupsPerWave]) {
+  bool big = false;
+#pragma unroll
+  for (int gq = 0; gq < kGroupsPerWave; ++gq)
+    big = big || fabsf(m[gq]) >= kSatLimit || (BM && fabsf(e[gq]) >= kSatLimit);
+  return wave_any(big);
+}
+
+template <int PV>
+__device__ __forceinline__ void saturate_p(PTile<PV>& P) {
+  if constexpr (PV == kPvFp8) {
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) P.w[kt] = e4m3x4_saturate(P.w[kt]);
+  }
 }
 
 // Rounds the p of keys 32g + 4kt .. +3 into P.  The e4m3 conversions overwrite both
@@ -351,6 +337,7 @@ __device__ __forceinline__ float softmax_group(v4i (&S)[8], float c, int nvalid,
     }
     store_p<PV>(P, kt, p);
   }
+  if (PV == kPvFp8 && wave_any(fabsf(m_new) >= kSatLimit || (BM && fabsf(e) >= kSatLimit))) saturate_p<PV>(P);
   lpart = alpha * lpart + lsum;
   m = m_new;
   return alpha;
@@ -417,6 +404,10 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
       for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
       store_p<PV>(P[gq], kt, p);
     }
+  }
+  if (PV == kPvFp8 && saturate_tile<BM>(m_new, e)) {
+#pragma unroll
+    for (int gq = 0; gq < G; ++gq) saturate_p<PV>(P[gq]);
   }
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
@@ -502,6 +493,10 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const uint8_t* 
       for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
       store_p<PV>(P[gq], kt, p);
     }
+  }
+  if (PV == kPvFp8 && saturate_tile<BM>(m_new, e)) {
+#pragma unroll
+    for (int gq = 0; gq < G; ++gq) saturate_p<PV>(P[gq]);
   }
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
@@ -602,16 +597,6 @@ struct IssuePriority {
     }
   }
 };
-
-// Maps the linear workgroup id to (head, query block) so that the workgroups one XCD
-// receives (ids x, x+8, x+16, ... go to XCD x) are consecutive query blocks of the same
-// heads and share that head's K/V tiles in the XCD's L2.
-__device__ __forceinline__ int xcd_remap(int id, int total) {
-  constexpr int kXcds = 8;
-  const int per = total / kXcds, rem = total % kXcds;
-  const int x = id % kXcds, idx = id / kXcds;
-  return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
-}
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -882,8 +867,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn_sparse(Attn
   attn_body<D, kPvFp8, false, false, true, PAIR>(a);
 }
 
-// Int32 S tiles through the same staging (LDS DMA, swizzle) and matrix-core code as
-// k_attn.
+// Int32 S tiles through the same staging (LDS DMA, swizzle), matrix-core code and
+// biased accumulator start as k_attn; the bias is subtracted on the way out.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict__ q_i8,
                                                   const int8_t* __restrict__ k_i8, int64_t npad,
@@ -901,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
   load_q<D>(q_i8 + bh * npad * D, qrow0, lane, qfr);
   __syncthreads();
   v4i S[G][8];
-  qk_tile<D>(klds, qfr, LaneOffsets<D>(lane), S, 0);
+  qk_tile<D>(klds, qfr, LaneOffsets<D>(lane), S, kSBiasBits);   // the attention kernel's accumulator start
   const int64_t ld = (int64_t)n_kv_tiles * kKvTile;
 #pragma unroll
   for (int gq = 0; gq < G; ++gq) {
@@ -910,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void k_debug_qk(const int8_t* __restrict_
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s_out[row * ld + (int64_t)blockIdx.x * kKvTile + 32 * g + 4 * kt + i] = S[gq][kt][i];
+        s_out[row * ld + (int64_t)blockIdx.x * kKvTile + 32 * g + 4 * kt + i] = S[gq][kt][i] - kSBiasBits;
   }
 }
 

@@ -81,6 +81,7 @@ def test_kernel_info_and_sizes(lib):
     (dict(N=(1 << 22) + 1), -2, "SAGE_MAX_TOKENS"),
     (dict(sm=float("nan")), -1, "sm_scale"),
     (dict(sm=-1.0), -1, "sm_scale"),
+    (dict(sm=0.0, ws=0), -4, "workspace is NULL"),    # 0 selects 1/sqrt(d): accepted
     (dict(q=A + 8), -3, "16-byte aligned"),
     (dict(ws=0), -4, "workspace is NULL"),
     (dict(ws=W + 64), -4, "256-byte aligned"),
@@ -202,3 +203,26 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_capi, "lib_path", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _capi.load()
+
+
+def test_binding_rejects_operands_of_another_mode():
+    # the prequant entry point takes mode-0 operands only, and a caller's operand dict
+    # must match the layout the library writes for the requested mode
+    import torch
+    from quantized_attention_diffusion_amd import _capi
+    with pytest.raises(ValueError, match="mode-0"):
+        _capi.sage_attn_fwd_prequant({"mode": _capi.SAGE_QK_PER_TOKEN})
+    B, H, N, d = 1, 2, 300, 64
+    cpu = torch.device("cpu")
+    good = _capi._alloc_quant(B, H, N, d, cpu, 0)
+    _capi._check_quant_out(good, B, H, N, d, cpu, 0)
+    with pytest.raises(ValueError, match="q_scale"):        # per-token scales need Npad entries
+        _capi._check_quant_out(good, B, H, N, d, cpu, _capi.SAGE_QK_PER_TOKEN)
+    with pytest.raises(ValueError, match="v_f8"):           # bf16 V needs 2 bytes per element
+        _capi._check_quant_out(dict(good, q_scale=_capi._alloc_quant(B, H, N, d, cpu, 2)["q_scale"],
+                                    k_scale=_capi._alloc_quant(B, H, N, d, cpu, 2)["k_scale"]),
+                               B, H, N, d, cpu, _capi.SAGE_QK_PER_TOKEN | _capi.SAGE_PV_BF16)
+    bad = dict(good)
+    del bad["k_mean"]
+    with pytest.raises(ValueError, match="k_mean"):
+        _capi._check_quant_out(bad, B, H, N, d, cpu, 0)

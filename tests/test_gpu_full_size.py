@@ -19,7 +19,7 @@ import torch
 import oracle
 import workloads
 import quantized_attention_diffusion_amd as sage
-from gpu_helpers import require_gpu, to_np, compare_quant, check_attention
+from gpu_helpers import require_gpu, to_np, compare_quant, check_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +74,11 @@ def test_offsets_beyond_int32():
         qh, kh, vh = (t[b:b + 1, :, h:h + 1].float().cpu().numpy() for t in (q, k, v))
         ref = oracle.quantize(qh, kh, vh)
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=12, replace=False)]))
-        pipe = oracle.attention_pipeline(qh, kh, vh, rows=rows, quant=ref)
-        check_attention(to_np(out[b:b + 1, rows, h:h + 1, :]), pipe, f"int64 dense {(b, h)}")
+        check_oracle(to_np(out[b:b + 1, rows, h:h + 1, :]), f"int64 dense {(b, h)}", qh, kh, vh,
+                     rows=rows, quant=ref)
         _, tiles = oracle.select_tiles(ref, 0.25)
-        pipe_s = oracle.attention_pipeline(qh, kh, vh, rows=rows, quant=ref, tiles=tiles)
-        check_attention(to_np(sparse[b:b + 1, rows, h:h + 1, :]), pipe_s, f"int64 sparse {(b, h)}")
+        check_oracle(to_np(sparse[b:b + 1, rows, h:h + 1, :]), f"int64 sparse {(b, h)}", qh, kh, vh,
+                     rows=rows, quant=ref, tiles=tiles)
     del q, k, v, out, sparse
     torch.cuda.empty_cache()
 
@@ -117,12 +117,12 @@ def _full_size_parity(w):
         # attention output of sampled rows
         rows = np.unique(np.concatenate([[0, N - 1], np.arange(max(0, N - 5), N),
                                          rng.choice(N, size=N_ROWS, replace=False)]))
-        pipe = oracle.attention_pipeline(qh, kh, vh, kv_tile=T, rows=rows, quant=ref)
         o = to_np(out[:, rows, h:h + 1, :])
-        err = check_attention(o, pipe, f"{name} head {h}")
+        err, err32, pipe = check_oracle(o, f"{name} head {h}", qh, kh, vh, kv_tile=T, rows=rows, quant=ref)
         exact = oracle.attention_exact(qh, kh, vh, rows=rows)
         r_gpu, r_pipe = oracle.rel_l2(o, exact), oracle.rel_l2(pipe, exact)
-        print(f"    head {h}: max|gpu-pipe| = {err:.2e}  relL2 gpu {r_gpu:.4f}  pipe {r_pipe:.4f}", flush=True)
+        print(f"    head {h}: max|gpu-pipe| = {err:.2e} (fp32 reading {err32:.2e})  relL2 gpu {r_gpu:.4f}  "
+              f"pipe {r_pipe:.4f}", flush=True)
         assert r_gpu <= r_pipe + 0.002
 
 
@@ -139,11 +139,63 @@ def test_full_size_quality_mode(name, per_token):
     for h in sorted({0, int(rng.integers(1, w.H))}):
         qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=N_ROWS, replace=False)]))
-        pipe = oracle.attention_pipeline(qh, kh, vh, kv_tile=128, rows=rows, fp8_p=False,
-                                         bf16_p=True, fp8_v=False, block=1 if per_token else 64)
         o = to_np(out[:, rows, h:h + 1, :])
-        err = check_attention(o, pipe, f"{name} quality head {h}")
+        err, _, pipe = check_oracle(o, f"{name} quality head {h}", qh, kh, vh, kv_tile=128, rows=rows,
+                                    fp8_p=False, bf16_p=True, fp8_v=False, block=1 if per_token else 64)
         exact = oracle.attention_exact(qh, kh, vh, rows=rows)
         r_gpu, r_pipe = oracle.rel_l2(o, exact), oracle.rel_l2(pipe, exact)
         print(f"    head {h}: max|gpu-pipe| = {err:.2e}  relL2 gpu {r_gpu:.4f}  pipe {r_pipe:.4f}", flush=True)
+        assert r_gpu <= r_pipe + 0.002
+
+
+# The quality options at full size and on long grids.  Grids of more than 4 x (compute
+# units) workgroups launch the plain instances of the attention kernel (the shorter
+# ones the workgroup-pair instances), so these sizes run the instances the bench times.
+MODES = {  # name: (per_token, k_block_mean)
+    "fp8_per_token": (True, False),
+    "block_mean_block64": (False, True),
+    "block_mean_per_token": (True, True),
+}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", ["sweep16k", "stress", "d64_long"])
+def test_full_size_fp8_modes(name, mode):
+    per_token, kbm = MODES[mode]
+    w = (workloads.Workload("d64_long", B=2, H=8, N=16384 - 37, d=64, seed=6) if name == "d64_long"
+         else workloads.get(name))
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    grid = w.B * w.H * (sage.sage_padded_tokens(w.N) // sage.sage_kernel_info()["block_m"])
+    assert grid > 4 * cus, "the case must launch the plain (long-grid) instance"
+    print(f"[full {mode}] {name} B={w.B} H={w.H} N={w.N} d={w.d} grid={grid}", flush=True)
+    q, k, v = workloads.make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = sage.sage_attn_fwd_ex(qd, kd, vd, per_token=per_token, k_block_mean=kbm)
+    gq = sage.sage_quant_qk_ex(qd, kd, vd, sage.mode_bits("fp8", per_token=per_token, k_block_mean=kbm))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2024)
+    N = w.N
+    nb = -(-N // 64)
+    for b, h in sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(1, w.H - 1)))}):
+        qh, kh, vh = (t[b:b + 1, :, h:h + 1, :].float().numpy() for t in (q, k, v))
+        ref = oracle.quantize(qh, kh, vh, block=1 if per_token else 64, k_block_mean=kbm)
+        # scales (and block means) bit-exact for the whole head, codes on sampled rows
+        nsc = N if per_token else nb
+        for nm in ("q", "k"):
+            sc = gq[f"{nm}_scale"][b, h].cpu().numpy()
+            assert np.array_equal(sc[:nsc].view(np.uint32), ref[f"{nm}_scale"][0, 0].view(np.uint32)), nm
+        if kbm:
+            km = gq["k_mean"][b, h].float().cpu().numpy()
+            assert np.array_equal(km[:nb].view(np.uint32), ref["k_bmean"][0, 0].view(np.uint32))
+        rows = np.unique(np.concatenate([[0, N - 1], np.arange(max(0, N - 5), N),
+                                         rng.choice(N, size=N_ROWS, replace=False)]))
+        for nm in ("q", "k"):
+            codes = gq[f"{nm}_i8"][b, h].cpu().numpy()
+            assert np.array_equal(codes[rows], ref[f"{nm}_i8"][0, 0][rows]), f"{nm}_i8 rows differ"
+        o = to_np(out[b:b + 1, rows, h:h + 1, :])
+        err, err32, pipe = check_oracle(o, f"{name} {mode} ({b}, {h})", qh, kh, vh, rows=rows, quant=ref)
+        exact = oracle.attention_exact(qh, kh, vh, rows=rows)
+        r_gpu, r_pipe = oracle.rel_l2(o, exact), oracle.rel_l2(pipe, exact)
+        print(f"    ({b}, {h}): max|gpu-pipe| = {err:.2e} (fp32 reading {err32:.2e})  relL2 gpu {r_gpu:.4f}  "
+              f"pipe {r_pipe:.4f}", flush=True)
         assert r_gpu <= r_pipe + 0.002

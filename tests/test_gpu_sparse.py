@@ -10,7 +10,7 @@ import torch
 import oracle
 import workloads
 import quantized_attention_diffusion_amd as sage
-from gpu_helpers import require_gpu, to_np, random_qkv, check_attention
+from gpu_helpers import require_gpu, to_np, random_qkv, check_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -82,8 +82,8 @@ def test_sparse_attention_matches_oracle_pipeline(case, density):
     o = to_np(out)
     ref = oracle.quantize(_np(q), _np(k), _np(v))
     _, tiles = oracle.select_tiles(ref, density)
-    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), quant=ref, tiles=tiles)
-    err = check_attention(o, pipe, f"{_case_id(case)} density {density}")
+    err, _, _ = check_oracle(o, f"{_case_id(case)} density {density}", _np(q), _np(k), _np(v),
+                             quant=ref, tiles=tiles)
     print(f"    max|gpu-pipe| = {err:.2e}", flush=True)
 
 
@@ -158,8 +158,8 @@ def test_full_size_sparse(name, density, n_heads):
         if h in heads[:2]:
             _, tiles = oracle.select_tiles(ref, density)
             rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=24, replace=False)]))
-            pipe = oracle.attention_pipeline(qh, kh, vh, quant=ref, rows=rows, tiles=tiles)
-            err = check_attention(to_np(out[:, rows, h:h + 1, :]), pipe, f"{name} head {h}")
+            err, _, _ = check_oracle(to_np(out[:, rows, h:h + 1, :]), f"{name} head {h}", qh, kh, vh,
+                                     quant=ref, rows=rows, tiles=tiles)
             print(f"    head {h}: max|gpu-pipe| = {err:.2e}", flush=True)
 
 
@@ -169,5 +169,5 @@ def test_sparse_with_a_given_sm_scale():
     out = sage.sage_attn_fwd_sparse(q.cuda(), k.cuda(), v.cuda(), 0.5, sm_scale=sm)
     ref = oracle.quantize(_np(q), _np(k), _np(v))
     _, tiles = oracle.select_tiles(ref, 0.5)      # the selection does not depend on sm_scale
-    pipe = oracle.attention_pipeline(_np(q), _np(k), _np(v), sm_scale=sm, quant=ref, tiles=tiles)
-    check_attention(to_np(out), pipe, "sparse sm_scale 0.05")
+    check_oracle(to_np(out), "sparse sm_scale 0.05", _np(q), _np(k), _np(v), sm_scale=sm, quant=ref,
+                 tiles=tiles)

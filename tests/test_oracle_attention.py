@@ -447,3 +447,28 @@ def test_fp32_and_fp64_readings_agree_on_the_workloads():
         a = attention_pipeline(q, k, v, quant=quant, rows=rows)
         b = attention_pipeline(q, k, v, quant=quant, rows=rows, arith="fp32")
         assert np.abs(a - b).max() < 1e-4, w.name
+
+
+def test_code_margin_covers_the_fp32_reading():
+    # the two readings differ only through P codes that an fp32 evaluation may round the
+    # other way; the plain reading's margin bounds that: |fp64 - fp32| <= margin + 1e-5
+    # everywhere, in every mode, on inputs whose outlier channels and block means give
+    # logits of several hundred (where codes do flip)
+    w = workloads.Workload("case", B=2, H=3, N=200, d=128, outliers=2, seed=7)
+    q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
+    flipped = False
+    for kw in [dict(block=64), dict(block=1), dict(block=64, k_block_mean=True),
+               dict(block=1, k_block_mean=True)]:
+        quant = oracle.quantize(q, k, v, **kw)
+        for pk in [dict(), dict(fp8_p=False, bf16_p=True, fp8_v=False)]:
+            if "k_block_mean" in kw and pk:
+                continue
+            a, mg = attention_pipeline(q, k, v, quant=quant, code_margin=True, **pk)
+            b = attention_pipeline(q, k, v, quant=quant, arith="fp32", **pk)
+            assert (np.abs(a - b) <= mg + 1e-5).all(), (kw, pk)
+            flipped |= bool((np.abs(a - b) > 1e-4).any())
+    assert flipped                       # the case does exercise code flips
+    # with P unrounded no code can flip: the margin is zero
+    quant = oracle.quantize(q, k, v)
+    _, mg = attention_pipeline(q, k, v, quant=quant, code_margin=True, fp8_p=False, fp8_v=False)
+    assert not mg.any()
