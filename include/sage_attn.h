@@ -179,6 +179,24 @@ int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
                   void* workspace, size_t workspace_bytes);
 
 /*
+ * sage_attn_fwd_noalloc - sage_attn_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace in a device array of
+ * SAGE_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on until
+ * the process ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Shapes whose sage_workspace_bytes() exceed that size return
+ * SAGE_EWORKSPACE.  Every call on one device shares the array: calls that can run
+ * concurrently on the same device (different streams, or several host threads) race
+ * and must be serialised by the caller.  Other arguments and status codes as for
+ * sage_attn_fwd; the first call on a device also resolves the array's address there
+ * (SAGE_EHIP if that fails).
+ */
+#define SAGE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sage_attn_fwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                          int B, int H, int N, int d, float sm_scale,
+                          const sage_strides strides[4], void* stream);
+
+/*
  * sage_attn_fwd_ex - sage_attn_fwd with quality options.  The pages note that
  * quantised attention schemes offer a quality-first setting beside the speed-first
  * one (bjdmk page "GitHub榜单静默期：Attention优化从架构转向推理加速", section 4.3) and

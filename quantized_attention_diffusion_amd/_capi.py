@@ -12,6 +12,7 @@ __all__ = ["SageError", "lib_path", "load", "sage_last_error", "sage_kernel_info
            "sage_padded_tokens", "sage_workspace_bytes", "sage_workspace_bytes_ex",
            "sage_quant_scratch_bytes", "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd",
            "sage_attn_fwd_ex", "sage_quant_qk_ex", "sage_debug_qk_i32", "sage_debug_e4m3",
+           "sage_attn_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "EXPORTS", "STATUS", "SAGE_PV_FP8", "SAGE_PV_BF16", "SAGE_QK_PER_TOKEN",
            "SAGE_K_BLOCK_MEAN", "mode_bits"]
 
@@ -26,7 +27,9 @@ EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
            "sage_quant_qk", "sage_quant_qk_ex", "sage_attn_fwd_prequant", "sage_attn_fwd",
            "sage_attn_fwd_ex", "sage_select_scratch_bytes", "sage_block_select",
            "sage_workspace_bytes_sparse", "sage_attn_fwd_sparse", "sage_debug_qk_i32",
-           "sage_debug_e4m3"]
+           "sage_debug_e4m3", "sage_attn_fwd_noalloc"]
+
+NOALLOC_SCRATCH_BYTES = 64 << 20        # SAGE_NOALLOC_SCRATCH_BYTES
 
 SAGE_PV_FP8, SAGE_PV_BF16, SAGE_QK_PER_TOKEN, SAGE_K_BLOCK_MEAN = 0, 1, 2, 4
 
@@ -86,6 +89,8 @@ _SIGS = {
                                   ctypes.POINTER(sage_strides), ctypes.c_float, _P, _P, _SZ]),
     "sage_debug_qk_i32": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "sage_debug_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
+    "sage_attn_fwd_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
+                                   ctypes.POINTER(sage_strides), _P]),
 }
 
 _lib = None
@@ -319,6 +324,25 @@ def sage_attn_fwd_ex(q, k, v, out: torch.Tensor | None = None, sm_scale: float |
         _check(load().sage_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                        B, H, N, d, sm, strides, mode, _stream(dev),
                                        workspace.data_ptr(), workspace.numel()))
+    return out
+
+
+def sage_attn_fwd_noalloc(q, k, v, out: torch.Tensor, sm_scale: float | None = None,
+                          layout: str = "bnhd") -> torch.Tensor:
+    """sage_attn_fwd without a workspace argument: the library's own device array
+    serves (at most NOALLOC_SCRATCH_BYTES of workspace; calls on one device must not
+    overlap).  ``out`` is the caller's; nothing is allocated."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _bf16_cuda(n, t)
+    (B, H, N, d), sq = _dims(q, layout)
+    dk, sk = _dims(k, layout)
+    dv, sv = _dims(v, layout)
+    do, so = _dims(out, layout)
+    if dk != (B, H, N, d) or dv != (B, H, N, d) or do != (B, H, N, d):
+        raise ValueError("q, k, v and out must have the same shape")
+    strides = (sage_strides * 4)(sq, sk, sv, so)
+    _check(load().sage_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        B, H, N, d, _scale_arg(sm_scale), strides, _stream(q.device)))
     return out
 
 

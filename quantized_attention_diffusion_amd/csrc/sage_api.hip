@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/sage_attn.h"
 #include "sage_internal.h"
@@ -338,10 +339,10 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
 
 // The whole path; with `sparse` the tile selection runs between the quantisation and
 // the attention, on the selection region that follows the mode-0 layout.
-static int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
-                         int B, int H, int N, int d, float sm_scale,
-                         const sage_strides strides[4], int mode, bool sparse, float density,
-                         void* stream, void* workspace, size_t workspace_bytes) {
+// Every check of the whole path that does not concern the workspace.
+static int validate_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                        int B, int H, int N, int d, float sm_scale,
+                        const sage_strides strides[4], int mode, bool sparse, float density) {
   if (int rc = check_mode(mode)) return rc;
   if (sparse) {
     if (int rc = check_sparse(B, H, N, d, density)) return rc;
@@ -356,7 +357,18 @@ static int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v
   for (int i = 0; i < 3; ++i)
     if (overlaps(eo, extent(ins[i], strides[i], B, H, N, d)))
       return fail(SAGE_EINVAL, "out overlaps %s", names[i]);
+  return resolve_sm_scale(sm_scale, d);
+}
+
+static int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                         int B, int H, int N, int d, float sm_scale,
+                         const sage_strides strides[4], int mode, bool sparse, float density,
+                         void* stream, void* workspace, size_t workspace_bytes) {
+  if (int rc = validate_fwd(q, k, v, out, B, H, N, d, sm_scale, strides, mode, sparse, density)) return rc;
   if (int rc = resolve_sm_scale(sm_scale, d)) return rc;
+  const void* ins[3] = {q, k, v};
+  const char* names[3] = {"q", "k", "v"};
+  const Extent eo = extent(out, strides[3], B, H, N, d);
   const QuantLayout L = layout(B, H, N, d, mode);
   const SelectLayout SL = select_layout(B, H, N, d);
   const size_t need = workspace_size(L) +
@@ -522,4 +534,55 @@ SAGE_EXPORT int sage_debug_e4m3(const float* x, uint8_t* codes, int64_t n, void*
   if (!x || !codes) return fail(SAGE_EINVAL, "x and codes must not be NULL");
   if (n > ((int64_t)1 << 40)) return fail(SAGE_EUNSUPPORTED, "n too large");
   return launch_status(sage::launch_debug_e4m3(x, codes, n, (hipStream_t)stream), "debug_e4m3");
+}
+
+// ---------------------------------------------------------------------------------------
+// sage_attn_fwd_noalloc: sage_attn_fwd with the workspace in a file-scope device array,
+// for callers that cannot allocate.  Each device holds its own copy of `scratch` (from
+// the first load of the library on it until the process ends); host code uses only the
+// device address hipGetSymbolAddress returns for the current device, resolved once per
+// device on the first call there.  Every call on a device shares its copy: calls that
+// can run concurrently on one device race.  No kernel of the path needs the workspace to
+// start zeroed (each writes every byte it later reads), so nothing is cleared.
+namespace {
+constexpr size_t kNoAllocBytes = (size_t)SAGE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+static int device_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SAGE_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SAGE_EUNSUPPORTED, "device %d is beyond the %d the no-allocation entry point tracks", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SAGE_EHIP, "hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+
+SAGE_EXPORT int sage_attn_fwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                                      int B, int H, int N, int d, float sm_scale,
+                                      const sage_strides strides[4], void* stream) {
+  if (int rc = validate_fwd(q, k, v, out, B, H, N, d, sm_scale, strides, 0, false, 1.0f)) return rc;
+  const size_t need = workspace_size(layout(B, H, N, d));
+  if (need > kNoAllocBytes)
+    return fail(SAGE_EWORKSPACE,
+                "B=%d H=%d N=%d d=%d needs %zu bytes of workspace; the no-allocation entry point holds %zu "
+                "(use sage_attn_fwd with a caller-owned workspace)", B, H, N, d, need, kNoAllocBytes);
+  void* ws = nullptr;
+  if (int rc = device_scratch(&ws)) return rc;
+  return attn_fwd_impl(q, k, v, out, B, H, N, d, sm_scale, strides, 0, false, 1.0f, stream, ws, kNoAllocBytes);
 }

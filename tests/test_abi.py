@@ -226,3 +226,19 @@ def test_binding_rejects_operands_of_another_mode():
     del bad["k_mean"]
     with pytest.raises(ValueError, match="k_mean"):
         _capi._check_quant_out(bad, B, H, N, d, cpu, 0)
+
+
+def test_noalloc_entry_point_rejects_shapes_beyond_its_scratch(lib):
+    # host-side size check before any HIP call: 8K tokens x 24 heads need 76.6 MiB of
+    # workspace, more than the 64 MiB device array
+    from quantized_attention_diffusion_amd import _capi
+    from quantized_attention_diffusion_amd._capi import sage_strides
+    B, H, N, d = 1, 24, 8192, 128
+    assert _capi.sage_workspace_bytes(B, H, N, d) > _capi.NOALLOC_SCRATCH_BYTES
+    st = (sage_strides * 4)(*[_st(N * H * d, d, H * d)] * 4)
+    rc = lib.sage_attn_fwd_noalloc(A, B_, C, O, B, H, N, d, ctypes.c_float(0.0), st, None)
+    assert rc == -4 and "no-allocation" in _err(lib)
+    # argument errors come first, as for sage_attn_fwd
+    rc = lib.sage_attn_fwd_noalloc(0, B_, C, O, 1, 2, 100, 128, ctypes.c_float(0.0),
+                                   (sage_strides * 4)(*[_st(100 * 2 * 128, 128, 2 * 128)] * 4), None)
+    assert rc == -1 and "q is NULL" in _err(lib)
