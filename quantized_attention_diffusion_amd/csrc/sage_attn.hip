@@ -867,6 +867,340 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn_sparse(Attn
   attn_body<D, kPvFp8, false, false, true, PAIR>(a);
 }
 
+
+// =====================================================================================
+// 32x32 matrix-core body (d = 128, FP8 P.V, 64-token scales; dense and block-sparse).
+// One group of 32 queries per wave: S^T on v_mfma_i32_32x32x32_i8 (four 32-key
+// sub-tiles x four 32-channel slices), O^T on v_mfma_scale_f32_32x32x64_f8f6f4 (four
+// 32-channel tiles x two 64-key halves).  Lane (n, h) holds, for its query n, the 64
+// keys 64ps + 32h + 0 .. 31 (ps = 0, 1) of every tile (k32_row_key): 32 keys in each
+// 64-key scale block, so two key scales per lane; the row maximum combines the lane
+// pair n, n + 32 with one v_permlane32_swap.  The larger shapes spend fewer VALU issue
+// cycles next to the softmax of the other wave on the SIMD, and one query per lane
+// halves the per-tile bookkeeping (maximum, rescale test, partial row sum).
+// The per-element arithmetic is that of softmax_tile.
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+struct LaneOffsets32 {
+  int koff[4];            // K slice kk (sub-tile kt adds k32_subtile_offset(kt))
+  int voff[2][2];         // V half ps, 16-byte part (channel tile dt adds dt * 32 * 128)
+  __device__ __forceinline__ explicit LaneOffsets32(int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff[kk] = k32_read_offset(lane, kk);
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) voff[ps][x] = v32_read_offset(lane, ps, x);
+  }
+};
+
+struct DmaOffsets32 {
+  static constexpr int KPW = DmaShape<128>::KPW;
+  static constexpr int VPW = DmaShape<128>::VPW;
+  static constexpr int PER_TILE = KPW + VPW;
+  uint32_t koff[KPW];
+  uint32_t voff[VPW];
+  __device__ __forceinline__ DmaOffsets32(int wave, int lane, int64_t npad) {
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) koff[j] = k32_dma_src(wave, j, lane);
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) voff[j] = v32_dma_src(wave, j, lane, npad);
+  }
+  __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t r, int tile_off, uint8_t* klds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < KPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(klds + (wave * KPW + j) * 1024), 16, koff[j],
+                                               tile_off, 0, 0);
+  }
+  __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t r, int tile_off, uint8_t* vlds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < VPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(vlds + (wave * VPW + j) * 1024), 16, voff[j],
+                                               tile_off, 0, 0);
+  }
+};
+
+// Q operand of S^T: lane (n, h) holds bytes 32kk + 16h .. +15 of query row qrow0 + n.
+__device__ __forceinline__ void load_q32(const int8_t* __restrict__ qh, int qrow0, int lane, v4i (&qf)[4]) {
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const v4i*)(qh + (int64_t)(qrow0 + n) * 128 + 32 * kk + 16 * h);
+}
+
+// int32 S^T of the staged key tile: S[kt] register i = s0 + S(query n, key 64(kt/2) +
+// 32h + 16(kt%2) + i).  Consecutive products go to different accumulators.
+__device__ __forceinline__ void qk_tile32(const uint8_t* kbuf, const v4i (&qf)[4], const LaneOffsets32& lo,
+                                          v16i (&S)[4], const v16i& s0) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const v4i a = *(const v4i*)(kbuf + lo.koff[kk] + k32_subtile_offset(kt));
+      S[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[kk], kk == 0 ? s0 : S[kt], 0, 0, 0);
+    }
+}
+
+// acc[dt] += V^T(channels 32dt .. +31) . P^T over the tile's two 64-key halves
+// (consecutive products go to different accumulators).
+__device__ __forceinline__ void pv_tile32(const uint8_t* vbuf, const v8i (&P)[2], const LaneOffsets32& lo,
+                                          v16f (&acc)[4]) {
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const v4i a = *(const v4i*)(vbuf + lo.voff[ps][0] + dt * 32 * kKvTile);
+      const v4i b = *(const v4i*)(vbuf + lo.voff[ps][1] + dt * 32 * kKvTile);
+      const v8i vf = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, P[ps], acc[dt], 0, 0, 0, 0, 0, 0);
+    }
+}
+
+// Online-softmax update of the lane's query for one tile.  c[ps] = fp32(q factor *
+// k_scale of block ps).  When MASKED, keys at tile index >= nvalid get the logit -inf
+// (a lane whose c is 0 then uses x = 0, c = 1 for its valid keys, as softmax_group
+// does).  Produces P, updates m and the partial row sum, returns alpha.
+template <bool MASKED>
+__device__ __forceinline__ float softmax32(v16i (&S)[4], const float (&c_in)[2], int nvalid, int h,
+                                           float log2_pscale, float& m, float& lpart, v8i (&P)[2]) {
+  float c[2] = {c_in[0], c_in[1]};
+  float sl;
+  if constexpr (!MASKED) {
+    int xm[2];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      int a0 = max(S[2 * ps][0], S[2 * ps][1]);
+      int a1 = max(S[2 * ps + 1][0], S[2 * ps + 1][1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) {
+        a0 = max(max(a0, S[2 * ps][i]), S[2 * ps][i + 1]);
+        a1 = max(max(a1, S[2 * ps + 1][i]), S[2 * ps + 1][i + 1]);
+      }
+      xm[ps] = max(a0, a1);
+    }
+    // c >= 0 and rounding is monotone: the block's maximum logit is fp32(max S * c)
+    sl = fmaxf(s_to_f32(xm[0]) * c[0], s_to_f32(xm[1]) * c[1]);
+  } else {
+    sl = -INFINITY;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const bool zero_c = (c[ps] == 0.0f);
+      c[ps] = zero_c ? 1.0f : c[ps];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool valid = 64 * ps + 32 * h + 16 * u + i < nvalid;
+          const float x = valid ? (zero_c ? 0.0f : s_to_f32(S[2 * ps + u][i])) : -INFINITY;
+          S[2 * ps + u][i] = __builtin_bit_cast(int, x);     // S now holds the fp32 logit factor
+          sl = fmaxf(sl, x == -INFINITY ? -INFINITY : x * c[ps]);
+        }
+    }
+  }
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sl), __float_as_uint(sl), false, false);
+    sl = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float m_new = fmaxf(m, sl);
+  const float nb = log2_pscale - m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float p[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int v = S[2 * ps + u][4 * i4 + t];
+          const float x = MASKED ? __builtin_bit_cast(float, v) : s_to_f32(v);
+          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c[ps], nb));
+          ls[t] += p[t];
+        }
+        const int w = 4 * u + i4;          // P word: keys 4w .. 4w+3 of the half
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[ps][w], false);
+        P[ps][w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
+      }
+  if (wave_any(fabsf(m_new) >= kSatLimit)) {
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) P[ps][w] = e4m3x4_saturate(P[ps][w]);
+  }
+  lpart = alpha * lpart + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+  m = m_new;
+  return alpha;
+}
+
+template <bool SPARSE, bool PAIR>
+__device__ __forceinline__ void attn32_body(const AttnArgs& a) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * Ring<D>::STAGE];
+  const IssuePriority<PAIR> prio(a.cu_count);
+  if constexpr (PAIR) prio.base();
+  const int nqb = (int)(a.npad / kBlockM);
+  const int total = nqb * a.B * a.H;
+  const int work = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, total));
+  const int64_t bh = __builtin_amdgcn_readfirstlane(work / nqb);
+  const int qb = __builtin_amdgcn_readfirstlane(work % nqb);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int qrow0 = qb * kBlockM + wave * 32;
+  const int64_t nblk = a.npad / kQuantBlock;
+
+  const LaneOffsets32 lo(lane);
+  const DmaOffsets32 dma(wave, lane, a.npad);
+  const int8_t* kh = a.k_i8 + bh * a.npad * D;
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kh, a.npad * D);
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(a.v_f8 + bh * D * a.npad, (int64_t)D * a.npad);
+  typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef const __attribute__((address_space(4))) f32x2* const_f32x2_ptr;
+  const const_f32_ptr ksh = (const_f32_ptr)(a.k_scale + bh * nblk);
+  const int ntiles = (a.N + kKvTile - 1) / kKvTile;
+  const int tail = a.N - (ntiles - 1) * kKvTile;
+
+  int nvis = ntiles;
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const_i32_ptr kept = nullptr;
+  if constexpr (SPARSE) {
+    const int64_t row = bh * nqb + qb;
+    nvis = __builtin_amdgcn_readfirstlane(((const_i32_ptr)a.tile_count)[row]);
+    kept = (const_i32_ptr)a.tile_list + row * a.tiles_max;
+  }
+  auto tile_at = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(kept[i]);
+    else return i;
+  };
+  const bool last_masked = tail < kKvTile && tile_at(nvis - 1) == ntiles - 1;
+  const int nfull_vis = last_masked ? nvis - 1 : nvis;
+  static_assert(kStages == 2, "visit i uses stage i % 2 and copies visit i + 1 into the other");
+  const Ring<D> ring{smem};
+  auto copy_tile = [&](int i) {
+    if (i < nvis) {
+      const int t = tile_at(i);
+      dma.issue_k(k_rsrc, t * kKvTile * D, ring.kbuf(i), wave);
+      dma.issue_v(v_rsrc, t * kKvTile, ring.vbuf(i), wave);
+    }
+  };
+  copy_tile(0);
+
+  v4i qfr[4];
+  load_q32(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
+  const float qf = a.q_scale[bh * nblk + qrow0 / kQuantBlock] * a.log2e_scale;
+  float m = -INFINITY, lpart = 0.0f;
+  v16f acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+  v16i s0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s0[i] = kSBiasBits;
+  v16i S[4];
+  v8i P[2] = {};
+  auto scales = [&](int t, float (&c)[2]) {
+    const f32x2 k01 = *(const_f32x2_ptr)(ksh + 2 * t);
+    c[0] = qf * k01[0];
+    c[1] = qf * k01[1];
+  };
+  auto rescale32 = [&](float alpha) {
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+    }
+  };
+  // One visit: the barrier (its copies have landed; every wave is done with the other
+  // stage), the K operand reads and QK^T, then the next visit's copy into the other
+  // stage, the softmax, and P.V.  The compiler makes every LDS read that follows an LDS
+  // copy wait for that copy (it cannot tell the stages apart), so the copy is issued
+  // after the K reads: it overlaps the softmax, and the P.V reads' wait finds it done.
+  auto visit = [&](int i, bool masked) {
+    tile_barrier<0>();
+    prio.mfma();
+    qk_tile32(ring.kbuf(i), qfr, lo, S, s0);
+    prio.base();
+    copy_tile(i + 1);
+    float c[2];
+    scales(tile_at(i), c);
+    const float alpha = masked ? softmax32<true>(S, c, tail, h, a.log2_pscale, m, lpart, P)
+                               : softmax32<false>(S, c, kKvTile, h, a.log2_pscale, m, lpart, P);
+    rescale32(alpha);
+    prio.mfma();
+    pv_tile32(ring.vbuf(i), P, lo, acc);
+    prio.base();
+  };
+  for (int i = 0; i < nfull_vis; ++i) visit(i, false);
+  if (last_masked) visit(nvis - 1, true);
+
+  // epilogue: the row sum over the lane pair, normalise, V scale, bf16
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart), __float_as_uint(lpart), false, false);
+  const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  const float rl = 1.0f / l;
+  const int b = (int)(bh / a.H), hh = (int)(bh % a.H);
+  const int qrow = qrow0 + n;
+  if (qrow < a.N) {
+    uint16_t* orow = a.out + (int64_t)b * a.so.b + (int64_t)hh * a.so.h + (int64_t)qrow * a.so.n;
+    const float* vsh = a.v_scale + bh * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int c0 = 32 * dt + 8 * jj + 4 * h;
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = acc[dt][4 * jj + t] * vsh[c0 + t] * rl;
+        *(uint2*)(orow + c0) = make_uint2(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
+                                          f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16));
+      }
+  }
+}
+
+template <bool PAIR>
+__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn32(AttnArgs a) {
+  attn32_body<false, PAIR>(a);
+}
+
+template <bool PAIR>
+__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void k_attn32_sparse(AttnArgs a) {
+  attn32_body<true, PAIR>(a);
+}
+
+// Int32 S tiles through the 32x32 body's staging, swizzle, matrix-core code and biased
+// accumulator start (d = 128).
+__global__ __launch_bounds__(kThreads) void k_debug_qk32(const int8_t* __restrict__ q_i8,
+                                                    const int8_t* __restrict__ k_i8, int64_t npad,
+                                                    int64_t bh, int q_block, int kv_tile,
+                                                    int n_kv_tiles, int32_t* __restrict__ s_out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t klds[Lds<128>::KBYTES];
+  const int qb = q_block + blockIdx.y, kvt = kv_tile + blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int qrow0 = qb * kBlockM + wave * 32;
+  const DmaOffsets32 dma(wave, lane, npad);
+  dma.issue_k(make_rsrc(k_i8 + bh * npad * 128, npad * 128), kvt * kKvTile * 128, klds, wave);
+  v4i qfr[4];
+  load_q32(q_i8 + bh * npad * 128, qrow0, lane, qfr);
+  __syncthreads();
+  v16i s0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s0[i] = kSBiasBits;
+  v16i S[4];
+  qk_tile32(klds, qfr, LaneOffsets32(lane), S, s0);
+  const int64_t ld = (int64_t)n_kv_tiles * kKvTile;
+  const int64_t row = (int64_t)blockIdx.y * kBlockM + wave * 32 + n;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      s_out[row * ld + (int64_t)blockIdx.x * kKvTile + 64 * (kt >> 1) + 32 * h + 16 * (kt & 1) + i] =
+          S[kt][i] - kSBiasBits;
+}
+
 // Int32 S tiles through the same staging (LDS DMA, swizzle), matrix-core code and
 // biased accumulator start as k_attn; the bias is subtracted on the way out.
 template <int D>
@@ -932,6 +1266,20 @@ static void launch_attn_tok(const AttnArgs& a, unsigned grid, hipStream_t s) {
 
 template <int D>
 static void launch_attn_d(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if constexpr (D == 128) {
+    // the 32x32 body: FP8 P.V with 64-token scales, dense or block-sparse
+    if (a.pv == kPvFp8 && !a.tok && !a.k_bmean) {
+      const bool pair = pair_priorities(a, grid);
+      if (a.tile_list) {
+        if (pair) hipLaunchKernelGGL((k_attn32_sparse<true>), dim3(grid), dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((k_attn32_sparse<false>), dim3(grid), dim3(kThreads), 0, s, a);
+      } else {
+        if (pair) hipLaunchKernelGGL((k_attn32<true>), dim3(grid), dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((k_attn32<false>), dim3(grid), dim3(kThreads), 0, s, a);
+      }
+      return;
+    }
+  }
   if (a.tile_list) {
     if (pair_priorities(a, grid))
       hipLaunchKernelGGL((k_attn_sparse<D, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -971,6 +1319,11 @@ hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_
                            int64_t bh, int q_block, int kv_tile, int n_q_blocks,
                            int n_kv_tiles, int32_t* s_out, hipStream_t s) {
   const dim3 grid(n_kv_tiles, n_q_blocks);
+  if (d == 128) {
+    hipLaunchKernelGGL(k_debug_qk32, grid, dim3(kThreads), 0, s, q_i8, k_i8, npad, bh, q_block, kv_tile,
+                       n_kv_tiles, s_out);
+    return hipGetLastError();
+  }
   if (d == 64)
     hipLaunchKernelGGL(k_debug_qk<64>, grid, dim3(kThreads), 0, s, q_i8, k_i8, npad, bh, q_block,
                        kv_tile, n_kv_tiles, s_out);
@@ -1006,6 +1359,10 @@ template __global__ void k_attn<128, kPvBf16, false, false, false>(AttnArgs);
 template __global__ void k_attn<128, kPvBf16, false, false, true>(AttnArgs);
 template __global__ void k_attn<128, kPvBf16, true, false, false>(AttnArgs);
 template __global__ void k_attn<128, kPvBf16, true, false, true>(AttnArgs);
+template __global__ void k_attn32<false>(AttnArgs);
+template __global__ void k_attn32<true>(AttnArgs);
+template __global__ void k_attn32_sparse<false>(AttnArgs);
+template __global__ void k_attn32_sparse<true>(AttnArgs);
 template __global__ void k_attn_sparse<64, false>(AttnArgs);
 template __global__ void k_attn_sparse<64, true>(AttnArgs);
 template __global__ void k_attn_sparse<128, false>(AttnArgs);

@@ -112,6 +112,59 @@ __host__ __device__ __forceinline__ uint32_t v16_dma_src(int wave, int j, int la
   return (uint32_t)(ch * npad * 2 + (pc ^ v16swz(ch & 15)) * 16);
 }
 
+// ---- 32x32 matrix-core layout (d = 128): one group of 32 queries per wave ----
+// S^T = K.Q^T on v_mfma_i32_32x32x32_i8 over four 32-key sub-tiles kt: lane l holds
+// query n = l % 32 and, in register i = 4jj + t of sub-tile kt, output row
+// 8jj + 4h + t (h = l / 32).  Row j of sub-tile kt is mapped to the tile key
+// k32_row_key(kt, j), so lane (n, h) holds in sub-tiles 2ps and 2ps + 1 the 32
+// consecutive keys 64ps + 32h .. +31 (ps = 0, 1: the tile's two 64-key scale blocks),
+// register i of sub-tile 2ps + u being key 64ps + 32h + 16u + i: exactly the k bytes
+// 0 .. 31 of lane (n, h)'s P operand of O^T = V^T.P^T on
+// v_mfma_scale_f32_32x32x64_f8f6f4 over the same 64 keys.
+__host__ __device__ __forceinline__ int k32_row_key(int kt, int j) {
+  return 64 * (kt >> 1) + 32 * ((j >> 2) & 1) + 16 * (kt & 1) + 4 * (j >> 3) + (j & 3);
+}
+// Swizzles of the 32x32 operand reads (K tile [128 keys][128 B], V tile [128 channels]
+// [128 B]): a K read touches keys k32_row_key(kt, 0 .. 31), which vary key bits 0-3 and
+// 5, at chunk 2kk + h; a V read touches channels 32dt + 0 .. 31 at chunk 4ps + 2h +
+// half.  Both maps were chosen by timing all 2^15 linear maps of those five row bits
+// onto the three chunk bits on these read patterns (about one in eight runs at the
+// conflict-free rate); these are among the fastest.
+__host__ __device__ __forceinline__ int kswz32(int key) {
+  return ((key >> 5) & 1) | ((((key >> 1) ^ (key >> 3)) & 1) << 1) | (((key >> 2) & 1) << 2);
+}
+__host__ __device__ __forceinline__ int vswz32(int ch) {
+  return ((ch >> 3) & 1) | ((((ch >> 1) ^ (ch >> 3)) & 1) << 1) | ((((ch >> 2) ^ (ch >> 3)) & 1) << 2);
+}
+// LDS byte offset of lane `lane`'s 16-byte K operand read of sub-tile kt, 32-channel
+// slice kk: row n = lane % 32 of the operand, channel bytes 32kk + 16h .. +15.  The
+// swizzle reads key bits 1, 2, 3 and 5, which the sub-tile leaves alone, so sub-tile kt
+// adds (k32_row_key(kt, 0)) * 128.
+__host__ __device__ __forceinline__ int k32_read_offset(int lane, int kk) {
+  const int n = lane & 31, h = lane >> 5;
+  const int key = k32_row_key(0, n);
+  return key * 128 + 16 * ((2 * kk + h) ^ kswz32(key));
+}
+__host__ __device__ __forceinline__ int k32_subtile_offset(int kt) { return k32_row_key(kt, 0) * 128; }
+// LDS byte offset of the V operand read (channel tile 0, key half ps, 16-byte half
+// `half`): channel n, keys 64ps + 32h + 16half .. +15.  Channel tile dt adds dt * 32 * 128
+// (the swizzle reads channel bits 1-3 only).
+__host__ __device__ __forceinline__ int v32_read_offset(int lane, int ps, int half) {
+  const int n = lane & 31, h = lane >> 5;
+  return n * kKvTile + 16 * ((4 * ps + 2 * h + half) ^ vswz32(n));
+}
+// LDS DMA sources of the 32x32 layout (same instruction shape as DmaShape<128>).
+__host__ __device__ __forceinline__ uint32_t k32_dma_src(int wave, int j, int lane) {
+  const int pos = dma_lds_offset(wave, j, DmaShape<128>::KPW, lane);
+  const int key = pos / 128, pc = (pos % 128) / 16;
+  return (uint32_t)(key * 128 + (pc ^ kswz32(key)) * 16);
+}
+__host__ __device__ __forceinline__ uint32_t v32_dma_src(int wave, int j, int lane, int64_t npad) {
+  const int pos = dma_lds_offset(wave, j, DmaShape<128>::VPW, lane);
+  const int ch = pos / kKvTile, pc = (pos % kKvTile) / 16;
+  return (uint32_t)(ch * npad + (pc ^ vswz32(ch)) * 16);
+}
+
 // Maps the linear workgroup id to (head, query block) so that the workgroups one XCD
 // receives (ids x, x+8, x+16, ... go to XCD x) are consecutive query blocks of the same
 // heads and share that head's K/V tiles in the XCD's L2.  A permutation of [0, total).

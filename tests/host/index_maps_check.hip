@@ -11,7 +11,9 @@
 //   - the block-mean operands and the query-code operands name the same channels;
 //   - the side copies (key scales, block means) fill their LDS slots exactly once;
 //   - the epilogue writes each output channel once per query row, the masked-tile
-//     predicate keeps exactly the keys below N, and xcd_remap is a permutation.
+//     predicate keeps exactly the keys below N, and xcd_remap is a permutation;
+//   - the same for the 32x32 layout of d = 128 (one 32-query group per wave: every K
+//     and V byte of a tile is read once per wave).
 // Prints "ok" and exits 0, or prints the first failure and exits 1.
 #include <stdint.h>
 #include <stdio.h>
@@ -206,6 +208,91 @@ static void check_side_copies_and_epilogue() {
   for (int c = 0; c < D; ++c) CHECK(oc[c] == 1, "output channel %d written %d times", c, oc[c]);
 }
 
+// The 32x32 layout (d = 128): DMA with the 32x32 swizzles, K operand reads (row n of
+// sub-tile kt = key k32_row_key(kt, n), channel bytes 32kk + 16h ..), V operand reads
+// (channel 32dt + n, keys 64ps + 32h + 16half ..), and the S / P key correspondence.
+static void check_32x32(int64_t npad) {
+  const int KB = Lds<128>::KBYTES, VB = Lds<128>::VBYTES;
+  Tags kl(KB, 0), vl(VB, 0);
+  std::vector<char> kseen(KB, 0), vseen(VB, 0);
+  for (int w = 0; w < kWaves; ++w)
+    for (int i = 0; i < 64; ++i) {
+      for (int j = 0; j < DmaShape<128>::KPW; ++j) {
+        const int dst = dma_lds_offset(w, j, DmaShape<128>::KPW, i);
+        const uint32_t src = k32_dma_src(w, j, i);
+        CHECK(src % 16 == 0 && src + 16 <= (uint32_t)KB && dst + 16 <= KB, "32x32 K DMA out of the tile");
+        for (int b = 0; b < 16; ++b) {
+          CHECK(kl[dst + b] == 0 && !kseen[src + b], "32x32 K DMA byte copied twice");
+          kl[dst + b] = (int64_t)src + b + 1;
+          kseen[src + b] = 1;
+        }
+      }
+      for (int j = 0; j < DmaShape<128>::VPW; ++j) {
+        const int dst = dma_lds_offset(w, j, DmaShape<128>::VPW, i);
+        const uint32_t src = v32_dma_src(w, j, i, npad);
+        const int64_t ch = src / npad, key = src % npad;
+        CHECK(src % 16 == 0 && ch < 128 && key + 16 <= kKvTile && dst + 16 <= VB, "32x32 V DMA out of the tile");
+        CHECK((int64_t)src + (npad - kKvTile) + 16 <= (int64_t)128 * npad, "32x32 V DMA past the buffer");
+        for (int b = 0; b < 16; ++b) {
+          CHECK(vl[dst + b] == 0 && !vseen[ch * kKvTile + key + b], "32x32 V DMA byte copied twice");
+          vl[dst + b] = ch * kKvTile + key + b + 1;
+          vseen[ch * kKvTile + key + b] = 1;
+        }
+      }
+    }
+  for (int x = 0; x < KB; ++x) CHECK(kl[x] != 0, "32x32 K LDS byte %d never written", x);
+  for (int x = 0; x < VB; ++x) CHECK(vl[x] != 0, "32x32 V LDS byte %d never written", x);
+  Tags kr(KB, 0), vr(VB, 0);
+  for (int lane = 0; lane < 64; ++lane) {
+    const int n = lane & 31, h = lane >> 5;
+    for (int kt = 0; kt < 4; ++kt)
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = k32_read_offset(lane, kk) + k32_subtile_offset(kt);
+        CHECK(off % 16 == 0 && off >= 0 && off + 16 <= KB, "32x32 K read outside the tile");
+        const int key = k32_row_key(kt, n);
+        for (int b = 0; b < 16; ++b) {
+          CHECK(kl[off + b] == (int64_t)key * 128 + 32 * kk + 16 * h + b + 1,
+                "32x32 K read lane %d kt %d kk %d byte %d", lane, kt, kk, b);
+          kr[off + b]++;
+        }
+      }
+    for (int dt = 0; dt < 4; ++dt)
+      for (int ps = 0; ps < 2; ++ps)
+        for (int x = 0; x < 2; ++x) {
+          const int off = v32_read_offset(lane, ps, x) + dt * 32 * kKvTile;
+          CHECK(off % 16 == 0 && off >= 0 && off + 16 <= VB, "32x32 V read outside the tile");
+          for (int b = 0; b < 16; ++b) {
+            CHECK(vl[off + b] == (int64_t)(32 * dt + n) * kKvTile + 64 * ps + 32 * h + 16 * x + b + 1,
+                  "32x32 V read lane %d dt %d ps %d", lane, dt, ps);
+            vr[off + b]++;
+          }
+        }
+  }
+  for (int x = 0; x < KB; ++x) CHECK(kr[x] == 1, "32x32 K LDS byte %d read %lld times per wave", x, (long long)kr[x]);
+  for (int x = 0; x < VB; ++x) CHECK(vr[x] == 1, "32x32 V LDS byte %d read %lld times per wave", x, (long long)vr[x]);
+  // S^T output: register i = 4jj + t of sub-tile kt in lane half h is row 8jj + 4h + t,
+  // which must be key 64(kt/2) + 32h + 16(kt%2) + i: byte 16(kt%2) + i of the P operand
+  // of half kt/2, whose lane half h covers keys 64ps + 32h .. +31
+  for (int h = 0; h < 2; ++h)
+    for (int kt = 0; kt < 4; ++kt)
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+        CHECK(k32_row_key(kt, row) == 64 * (kt >> 1) + 32 * h + 16 * (kt & 1) + i, "32x32 S layout h %d kt %d i %d", h, kt, i);
+      }
+  // each sub-tile's 32 rows are 32 distinct keys, and the four sub-tiles cover the tile
+  std::vector<int> cover(128, 0);
+  for (int kt = 0; kt < 4; ++kt)
+    for (int j = 0; j < 32; ++j) cover[k32_row_key(kt, j)]++;
+  for (int key = 0; key < 128; ++key) CHECK(cover[key] == 1, "32x32 key %d covered %d times", key, cover[key]);
+  // epilogue: lane half h writes channels 32dt + 8jj + 4h + t
+  std::vector<int> oc(128, 0);
+  for (int h = 0; h < 2; ++h)
+    for (int dt = 0; dt < 4; ++dt)
+      for (int jj = 0; jj < 4; ++jj)
+        for (int t = 0; t < 4; ++t) oc[32 * dt + 8 * jj + 4 * h + t]++;
+  for (int c = 0; c < 128; ++c) CHECK(oc[c] == 1, "32x32 output channel %d written %d times", c, oc[c]);
+}
+
 static void check_tails_rows_and_remap() {
   for (int N = 1; N <= 1100; ++N) {
     const int ntiles = (N + kKvTile - 1) / kKvTile;
@@ -248,6 +335,7 @@ int main() {
     check_v<128>(npad);
     check_v16<64>(npad);
     check_v16<128>(npad);
+    check_32x32(npad);
   }
   check_side_copies_and_epilogue<64>();
   check_side_copies_and_epilogue<128>();
