@@ -25,9 +25,11 @@
 //   by LDS DMA (buffer_load_dwordx4 ... lds: no data registers, and the per-tile
 //   address advance is a scalar offset, so no vector instruction) and shared by the 4
 //   waves: speed mode double-buffers (K, V) stages, one tile ahead of use; quality mode
-//   double-buffers K and refills a single bf16 V buffer while S and the softmax of the
-//   same tile are computed.  Waits are counted (s_waitcnt vmcnt(n) + s_barrier), so a
-//   wave only waits for the copies it needs.
+//   double-buffers K and refills a single bf16 V buffer during the softmax of the same
+//   tile.  The copies of the next tile are issued after the K operand reads of the
+//   current one (the compiler makes an LDS read wait for every LDS copy issued before
+//   it), so they overlap the softmax.  Waits are counted (s_waitcnt vmcnt(n) +
+//   s_barrier), so a wave only waits for the copies it needs.
 //
 // Register layouts (16x16 matrix-core tiles; lane l, r = l % 16, g = l / 16)
 //   S^T = K . Q^T with v_mfma_i32_16x16x64_i8: the row operand is 16 keys, the column
@@ -79,19 +81,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
 }
 
 // Per-lane source offsets of the LDS DMA copies (computed once per kernel, sage_tiles.h):
-// the K tile copy of wave w, instruction j reads K + koff[j], the V tile copy V + voff[j]
-// (bytes, relative to the tile's first key), which lands at LDS offset
-// dma_lds_offset(w, j, PW, lane).
+// the K tile copy of wave w, instruction j reads K + koff0 + 1024 j (the K swizzle
+// leaves key bits 3 and 4, which j changes, alone: k_dma_src is affine in j, so one
+// register serves, the 1024 j going into the scalar offset, which moves the global
+// address only; the instruction's immediate offset would move the LDS address too),
+// the V tile copy V + voff[j] (bytes, relative to the tile's first key); copy j lands at
+// LDS offset dma_lds_offset(w, j, PW, lane).
 template <int D>
 struct DmaOffsets {
   static constexpr int KPW = DmaShape<D>::KPW;
   static constexpr int VPW = DmaShape<D>::VPW;
   static constexpr int PER_TILE = KPW + VPW;     // DMA instructions per wave per tile
-  uint32_t koff[KPW];
+  uint32_t koff0;
   uint32_t voff[VPW];
   __device__ __forceinline__ DmaOffsets(int wave, int lane, int64_t npad) {
-#pragma unroll
-    for (int j = 0; j < KPW; ++j) koff[j] = k_dma_src<D>(wave, j, lane);
+    koff0 = k_dma_src<D>(wave, 0, lane);
 #pragma unroll
     for (int j = 0; j < VPW; ++j) voff[j] = v_dma_src<D>(wave, j, lane, npad);
   }
@@ -99,8 +103,8 @@ struct DmaOffsets {
   __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t kbufr, int tile_off, uint8_t* klds, int wave) const {
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kbufr, (lds_ptr_t)(klds + (wave * KPW + j) * 1024), 16, koff[j],
-                                               tile_off, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kbufr, (lds_ptr_t)(klds + (wave * KPW + j) * 1024), 16, koff0,
+                                               tile_off + 1024 * j, 0, 0);
   }
   __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t vbufr, int tile_off, uint8_t* vlds, int wave) const {
 #pragma unroll
@@ -661,7 +665,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   const int qb = __builtin_amdgcn_readfirstlane(work % nqb);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, g = lane >> 4;
+  int r = lane & 15, g = lane >> 4;
+  // After the main loop the lane-derived indices are derived again from the lane id
+  // computed anew (mbcnt counts the lanes below this one), so that the compiler
+  // recomputes what the masked last tile and the epilogue need instead of keeping it in
+  // registers across the loop (the per-token block-residual instances would otherwise
+  // spill it).
+  auto refresh_lane = [&]() {
+    int l2 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l2));
+    r = l2 & 15;
+    g = l2 >> 4;
+  };
   const int qrow0 = qb * kBlockM + wave * (G * 16);
   const int64_t nblk = a.npad / kQuantBlock;
 
@@ -768,15 +783,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     for (int i = 0; i < kStages - 1; ++i) copy_tile(i);
     load_q<D>(a.q_i8 + bh * a.npad * D, qrow0, lane, qfr);
     init_state();
-    constexpr int KEEP = (kStages - 2) * (DmaOffsets<D>::PER_TILE + SIDE);
+    static_assert(kStages == 2, "visit i copies visit i + 1 into the other stage");
     for (int i = 0; i < nfull_vis; ++i) {
-      // visit i has landed once only the copies of the kStages-2 later visits may be in flight
-      if (i + kStages - 2 < nvis) tile_barrier<KEEP>();
-      else tile_barrier<0>();
-      copy_tile(i + kStages - 1);        // into the stage all waves finished in visit i-1
+      // visit i has landed, and every wave is done with the other stage (visit i-1)
+      tile_barrier<0>();
       prio.mfma();
       qk_tile<D>(ring.kbuf(i), qfr, lo, S, kSBiasBits);
       prio.base();
+      // The compiler makes every LDS read that follows an LDS copy wait for that copy,
+      // so the next visit's copy is issued after the K reads: it overlaps the softmax.
+      copy_tile(i + 1);
       softmax_step(tile_at(i), false);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
@@ -784,6 +800,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       pv_tile<D>(ring.vbuf(i), P, lo, acc);
       prio.base();
     }
+    refresh_lane();
     if (last_masked) {                   // last tile: keys >= N masked
       const int i = nvis - 1;
       tile_barrier<0>();
@@ -795,8 +812,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     }
   } else {
     // K double-buffered, one bf16 V buffer.  Step t: barrier (K(t) landed, every wave
-    // done with step t-1), copy V(t) and K(t+1), S and softmax of tile t, barrier (V(t)
-    // landed; K(t+1) may still be in flight), P.V of tile t.
+    // done with step t-1), S of tile t, copy V(t) and K(t+1), softmax of tile t, barrier
+    // (V(t) landed; K(t+1) may still be in flight), P.V of tile t.
     uint8_t* vbuf = smem + 2 * Lds<D>::KBYTES;
     auto kbuf = [&](int t) { return smem + (t & 1) * Lds<D>::KBYTES; };
     const LaneOffsets16<D> lo16(lane);
@@ -813,11 +830,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     init_state();
     auto step = [&](int t, bool masked) {
       tile_barrier<0>();
-      dma16.issue_v(v_rsrc, t * kKvTile * 2, vbuf, wave);
-      copy_k(t + 1);
       prio.mfma();
       qk_tile<D>(kbuf(t), qfr, lo, S, kSBiasBits);
       prio.base();
+      // copies issued after the K reads (see the FP8 loop): V(t) and K(t+1) overlap the softmax
+      dma16.issue_v(v_rsrc, t * kKvTile * 2, vbuf, wave);
+      copy_k(t + 1);
       softmax_step(t, masked);
 #pragma unroll
       for (int gq = 0; gq < G; ++gq) rescale<D>(acc[gq], alpha[gq]);
@@ -829,6 +847,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       prio.base();
     };
     for (int t = 0; t < nfull; ++t) step(t, false);
+    refresh_lane();
     if (nfull < ntiles) step(nfull, true);
   }
 

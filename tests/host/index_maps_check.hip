@@ -49,6 +49,8 @@ static void check_k() {
       for (int i = 0; i < 64; ++i) {
         const int dst = dma_lds_offset(w, j, DmaShape<D>::KPW, i);
         const uint32_t src = k_dma_src<D>(w, j, i);
+        // the kernel issues copy j from k_dma_src(w, 0, lane) + 1024 j
+        CHECK(src == k_dma_src<D>(w, 0, i) + 1024u * j, "d=%d K DMA source not affine in j", D);
         CHECK(src % 16 == 0 && src + 16 <= (uint32_t)KB, "d=%d K DMA source %u outside the tile", D, src);
         CHECK(dst >= 0 && dst + 16 <= KB, "d=%d K DMA destination %d outside the stage", D, dst);
         for (int b = 0; b < 16; ++b) {
