@@ -4,10 +4,16 @@ A step is one sage_attn_fwd call (quantisation pass + fused attention) over the
 seeded synthetic Flux-like workload (B=1, H=24, N=4608, d=128) with inputs resident in
 HBM.  Prints one JSON line: whole-step TOPS (4*B*H*N^2*d per step), the attention
 kernel's matrix-core roofline fraction, the quantisation pass's HBM rate, the same
-figures at N=16384 and N=65536, and the CPU oracle timed on a bounded sample.
+figures at N=8192, 16384, 32760 (40 heads) and 65536, and the CPU oracle timed on the
+whole Flux-like workload.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
-                [--no-cpu-baseline] [--pmc-run] [--sparse-run WORKLOADS]
+Before the W warm-up steps of a timed window the step runs untimed for --warm-seconds
+(default 0.5 s): the GPU's clocks ramp up over tens of milliseconds after an idle gap
+(the host-side set-up between measurements), and a short window right after one reads
+low.  The time spent is reported as "warm_s".
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S] [--workload NAME]
+                [--no-sweep] [--no-cpu-baseline] [--pmc-run] [--sparse-run WORKLOADS]
 """
 from __future__ import annotations
 
@@ -22,23 +28,27 @@ sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0        # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s), x1000
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
-SWEEP = ["sweep16k", "stress"]
+SWEEP = ["sweep8k", "sweep16k", "video", "stress"]
+MODE_SWEEP = ["sweep16k", "stress"]   # sweep workloads the optional modes are also timed on
 SWEEP_STEPS = 20          # timed steps per sweep workload
 COPY_BYTES = 1 << 30      # calibration copy of the counter runs
 ATTN_SOURCES = ["quantized_attention_diffusion_amd/csrc/sage_attn.hip",
                 "quantized_attention_diffusion_amd/csrc/sage_device.h",
                 "quantized_attention_diffusion_amd/csrc/sage_internal.h",
+                "quantized_attention_diffusion_amd/csrc/sage_tiles.h",
                 "quantized_attention_diffusion_amd/build.py"]          # its compiler flags
 
 
 def attn_kernel_name(w, info):
-    """The attention kernel the library launches for workload w: the workgroup-pair
+    """The attention kernel the library launches for workload w (FP8 P.V, 64-token
+    scales): the 32x32 body for d = 128, the 16x16 one for d = 64; the workgroup-pair
     priority instance when the grid is at most two rounds of two workgroups per compute
     unit, the plain one otherwise."""
     import torch
     grid = -(-w.N // info["block_m"]) * w.B * w.H
     cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    return "k_attn<%d, 0, false, false, %s>" % (w.d, "true" if grid <= 4 * cus else "false")
+    pair = "true" if grid <= 4 * cus else "false"
+    return f"k_attn32<{pair}>" if w.d == 128 else f"k_attn<{w.d}, 0, false, false, {pair}>"
 
 
 def _parse():
@@ -46,6 +56,8 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="untimed steps for this long before the warm-up steps of each timed window")
     ap.add_argument("--workload", default="flux_like")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -71,6 +83,25 @@ MODES = {"bf16_pv": dict(pv="bf16"),
          "fp8_pv_block_mean_k": dict(pv="fp8", k_block_mean=True)}
 
 
+def warm(fn, seconds: float) -> float:
+    """Runs fn untimed until `seconds` have passed (synchronising every 20 calls);
+    returns the time spent."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+WARM_S = 0.5              # set from --warm-seconds
+CPU_SHARE = 16            # worker processes at most: the host-core share of one GPU
+
+
 def measure_mode(w, steps, warmup, **opts):
     """Whole-step time of sage_attn_fwd_ex with options ``opts`` on workload w."""
     import torch
@@ -83,6 +114,7 @@ def measure_mode(w, steps, warmup, **opts):
     mode = sage.mode_bits(**opts)
     ws = torch.empty(sage.sage_workspace_bytes_ex(w.B, w.H, w.N, w.d, mode), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    warm(lambda: sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, **opts), WARM_S)
     for _ in range(warmup):
         sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, **opts)
     torch.cuda.synchronize(dev)
@@ -116,6 +148,7 @@ def measure_sparse(w, steps, warmup, density):
     out = torch.empty_like(q)
     ws = torch.empty(sage.sage_workspace_bytes_sparse(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    warm(lambda: sage.sage_attn_fwd_sparse(q, k, v, density, out=out, workspace=ws), WARM_S)
     for _ in range(warmup):
         sage.sage_attn_fwd_sparse(q, k, v, density, out=out, workspace=ws)
     torch.cuda.synchronize(dev)
@@ -150,6 +183,7 @@ def measure(w, steps, warmup):
         return torch.cuda.Event(enable_timing=True)
 
     # whole step
+    warm_s = warm(lambda: sage.sage_attn_fwd(q, k, v, out=out, workspace=ws), WARM_S)
     for _ in range(warmup):
         sage.sage_attn_fwd(q, k, v, out=out, workspace=ws)
     torch.cuda.synchronize(dev)
@@ -165,6 +199,7 @@ def measure(w, steps, warmup):
 
     # the two passes alone, each timed with events on the stream the library uses
     quant = sage.sage_quant_qk(q, k, v)
+    warm(lambda: (sage.sage_quant_qk(q, k, v, out=quant), sage.sage_attn_fwd_prequant(quant, out=out)), WARM_S)
     for _ in range(warmup):
         sage.sage_quant_qk(q, k, v, out=quant)
         sage.sage_attn_fwd_prequant(quant, out=out)
@@ -183,7 +218,7 @@ def measure(w, steps, warmup):
     attn_ms = e2.elapsed_time(e3) / steps
     del q, k, v, out, ws, quant
     torch.cuda.empty_cache()
-    return dict(step_ms=step_ms, wall_s=wall, quant_ms=quant_ms, attn_ms=attn_ms,
+    return dict(step_ms=step_ms, wall_s=wall, quant_ms=quant_ms, attn_ms=attn_ms, warm_s=warm_s,
                 tops=w.ops / (step_ms * 1e-3) / 1e12,
                 attn_tops=w.ops / (attn_ms * 1e-3) / 1e12,
                 quant_gbs=quant_bytes(w) / (quant_ms * 1e-3) / 1e9)
@@ -208,11 +243,11 @@ def _oracle_rows_worker(args):
         return time.perf_counter() - t0
 
 
-def cpu_baseline(w, rows_total: int = 3072):
-    """The CPU oracle (numpy) on a bounded sample of the workload: the full
-    quantisation of Q, K and V on one core, then the quantised attention of
-    ``rows_total`` query rows in every head, split over one worker process per host
-    core (up to 16), each with one BLAS thread.  Scaled to the whole workload
+def cpu_baseline(w, rows_total: int | None = None):
+    """The CPU oracle (numpy) on the workload: the full quantisation of Q, K and V on
+    one core, then the quantised attention of ``rows_total`` query rows (default: all
+    of them) in every head, split over one worker process per host core, each with one
+    BLAS thread.  With a sample of rows the time is scaled to the whole workload
     linearly in rows (rows are independent given the quantised K and V)."""
     import concurrent.futures as cf
     import multiprocessing as mp
@@ -222,14 +257,14 @@ def cpu_baseline(w, rows_total: int = 3072):
     import workloads
     from threadpoolctl import threadpool_limits
 
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores = max(1, min(CPU_SHARE, len(os.sched_getaffinity(0))))
     q, k, v = (t.float().numpy() for t in workloads.make_qkv(w))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         oracle.quantize(q, k, v)
         t_quant = time.perf_counter() - t0
     del q, k, v
-    rows_total = min(rows_total, w.N)
+    rows_total = w.N if rows_total is None else min(rows_total, w.N)
     rows = np.linspace(0, w.N - 1, rows_total).astype(np.int64)
     shares = [rows[i::cores].tolist() for i in range(cores)]
     ctx = mp.get_context("spawn")
@@ -240,8 +275,9 @@ def cpu_baseline(w, rows_total: int = 3072):
     return {"value": round(w.ops / est / 1e12, 8), "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": (f"{w.name}: full quantisation on 1 core ({t_quant:.1f} s), then attention of "
                        f"{rows_total} of {w.N} query rows in all {w.H} heads split over {cores} "
-                       f"processes ({t_rows:.1f} s wall, {sum(times):.1f} s CPU); scaled by rows "
-                       f"to {est:.0f} s per step; numpy, 1 BLAS thread per process")}
+                       f"processes ({t_rows:.1f} s wall, {sum(times):.1f} s CPU)"
+                       + (f"; scaled by rows to {est:.0f} s per step" if rows_total < w.N else
+                          f": {est:.1f} s per step") + "; numpy, 1 BLAS thread per process")}
 
 
 def kernel_source_hash() -> str:
@@ -330,6 +366,8 @@ def main():
         sys.exit(2)
     import workloads
 
+    global WARM_S
+    WARM_S = max(0.0, args.warm_seconds)
     w = workloads.get(args.workload)
     # The CPU baseline runs first, in worker processes started before this process
     # touches the GPU.
@@ -366,7 +404,7 @@ def main():
                            "mfma_util": round(rs["attn_tops"] / PEAK_TOPS, 4),
                            "quant_ms": round(rs["quant_ms"], 4),
                            "quant_gbs": round(rs["quant_gbs"], 1)}
-        for name in SWEEP + [w.name]:
+        for name in MODE_SWEEP + [w.name]:
             wq = workloads.get(name)
             print(f"[bench] optional modes {name} N={wq.N}", file=sys.stderr, flush=True)
             st, wu = (args.steps, args.warmup) if name == w.name else (SWEEP_STEPS, 2)
@@ -385,6 +423,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_s": round(r["warm_s"], 3),
         "ms_per_step": round(r["step_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
