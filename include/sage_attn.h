@@ -272,15 +272,35 @@ int sage_attn_fwd_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          void* workspace, size_t workspace_bytes);
 
 /*
+ * sage_density_schedule - the density of sampling step `step` of `n_steps` for
+ * sage_attn_fwd_sparse when it moves from sparse early to dense late over a sampling
+ * run (sd114.wiki page "ComfyUI-sol-attn", 核心亮点 item 4; the page gives no curve).
+ * Reading: linear in the step index, tau = fp32(tau_start + (tau_end - tau_start) *
+ * step / (n_steps - 1)) evaluated in fp64, so step 0 gets tau_start and the last step
+ * tau_end; a run of one step gets tau_end.  Host only (no GPU call).  Requires
+ * 0 <= step < n_steps, finite tau_start and tau_end > 0, tau non-NULL (else
+ * SAGE_EINVAL; *tau is then left unchanged).
+ */
+int sage_density_schedule(int step, int n_steps, float tau_start, float tau_end, float* tau);
+
+/*
  * sage_debug_qk_i32 - diagnostic: the exact int32 S = Q8.K8^T tiles of head (b, h),
- * computed by the same staging and matrix-core code as the attention kernel.
- * Covers query rows [q_block*block_m, (q_block+n_q_blocks)*block_m) and keys
- * [kv_tile*T, (kv_tile+n_kv_tiles)*T) of the padded operands; s_out is int32,
- * row-major [n_q_blocks*block_m][n_kv_tiles*T].  Tiles must lie inside Npad.
+ * computed by the same staging, LDS layout, matrix-core code and accumulator start as
+ * the attention kernel of mode 0.  Covers query rows [q_block*block_m,
+ * (q_block+n_q_blocks)*block_m) and keys [kv_tile*T, (kv_tile+n_kv_tiles)*T) of the
+ * padded operands; s_out is int32, row-major [n_q_blocks*block_m][n_kv_tiles*T].
+ * Tiles must lie inside Npad.  q_i8/k_i8: device, 256-byte aligned, the layout of
+ * sage_quant_qk; s_out: device, 16-byte aligned, caller-owned.
+ * sage_debug_qk_i32_ex - the same through the attention body that sage_attn_fwd_ex
+ * launches for `mode` (SAGE_* bits): at d = 128 the 32x32 matrix-core body for mode 0
+ * and the 16x16 body for every other mode; at d = 64 the 16x16 body.
  */
 int sage_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
                       int b, int h, int q_block, int kv_tile, int n_q_blocks, int n_kv_tiles,
                       int32_t* s_out, void* stream);
+int sage_debug_qk_i32_ex(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                         int b, int h, int q_block, int kv_tile, int n_q_blocks, int n_kv_tiles,
+                         int mode, int32_t* s_out, void* stream);
 
 /*
  * sage_debug_e4m3 - diagnostic: the device fp32 -> e4m3 conversion the quantisation

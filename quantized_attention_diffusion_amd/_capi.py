@@ -11,9 +11,10 @@ import torch
 __all__ = ["SageError", "lib_path", "load", "sage_last_error", "sage_kernel_info",
            "sage_padded_tokens", "sage_workspace_bytes", "sage_workspace_bytes_ex",
            "sage_quant_scratch_bytes", "sage_quant_qk", "sage_attn_fwd_prequant", "sage_attn_fwd",
-           "sage_attn_fwd_ex", "sage_quant_qk_ex", "sage_debug_qk_i32", "sage_debug_e4m3",
-           "sage_attn_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "EXPORTS", "STATUS", "SAGE_PV_FP8", "SAGE_PV_BF16", "SAGE_QK_PER_TOKEN",
+           "sage_attn_fwd_ex", "sage_quant_qk_ex", "sage_debug_qk_i32", "sage_debug_qk_i32_ex", "sage_debug_e4m3",
+           "sage_select_scratch_bytes", "sage_block_select", "sage_workspace_bytes_sparse",
+           "sage_attn_fwd_sparse", "sage_density_schedule", "sage_attn_fwd_noalloc",
+           "NOALLOC_SCRATCH_BYTES", "EXPORTS", "STATUS", "SAGE_PV_FP8", "SAGE_PV_BF16", "SAGE_QK_PER_TOKEN",
            "SAGE_K_BLOCK_MEAN", "mode_bits"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,8 @@ EXPORTS = ["sage_last_error", "sage_kernel_info", "sage_padded_tokens",
            "sage_quant_qk", "sage_quant_qk_ex", "sage_attn_fwd_prequant", "sage_attn_fwd",
            "sage_attn_fwd_ex", "sage_select_scratch_bytes", "sage_block_select",
            "sage_workspace_bytes_sparse", "sage_attn_fwd_sparse", "sage_debug_qk_i32",
-           "sage_debug_e4m3", "sage_attn_fwd_noalloc"]
+           "sage_debug_qk_i32_ex", "sage_debug_e4m3", "sage_attn_fwd_noalloc",
+           "sage_density_schedule"]
 
 NOALLOC_SCRATCH_BYTES = 64 << 20        # SAGE_NOALLOC_SCRATCH_BYTES
 
@@ -88,7 +90,9 @@ _SIGS = {
     "sage_attn_fwd_sparse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
                                   ctypes.POINTER(sage_strides), ctypes.c_float, _P, _P, _SZ]),
     "sage_debug_qk_i32": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "sage_debug_qk_i32_ex": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "sage_debug_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
+    "sage_density_schedule": (_I, [_I, _I, ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float)]),
     "sage_attn_fwd_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float,
                                    ctypes.POINTER(sage_strides), _P]),
 }
@@ -381,6 +385,15 @@ def sage_block_select(quant: dict, density: float, return_importance: bool = Fal
     return count, lists, imp
 
 
+def sage_density_schedule(step: int, n_steps: int, tau_start: float, tau_end: float = 1.0) -> float:
+    """Density of sampling step ``step`` of ``n_steps``, moving linearly from tau_start
+    (first step) to tau_end (last step); see the C header."""
+    tau = ctypes.c_float(0.0)
+    _check(load().sage_density_schedule(int(step), int(n_steps), ctypes.c_float(tau_start),
+                                        ctypes.c_float(tau_end), ctypes.byref(tau)))
+    return tau.value
+
+
 def sage_attn_fwd_sparse(q, k, v, density: float, out: torch.Tensor | None = None,
                          sm_scale: float | None = None, layout: str = "bnhd",
                          workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -420,6 +433,19 @@ def sage_debug_qk_i32(q_i8, k_i8, N: int, b: int, h: int, q_block: int, kv_tile:
     _check(load().sage_debug_qk_i32(q_i8.data_ptr(), k_i8.data_ptr(), B, H, N, d, b, h,
                                     q_block, kv_tile, n_q_blocks, n_kv_tiles, s.data_ptr(),
                                     _stream(q_i8.device)))
+    return s
+
+
+def sage_debug_qk_i32_ex(q_i8, k_i8, N: int, b: int, h: int, q_block: int, kv_tile: int,
+                         n_q_blocks: int = 1, n_kv_tiles: int = 1, mode: int = 0) -> torch.Tensor:
+    """sage_debug_qk_i32 through the attention body that ``mode`` (SAGE_* bits) selects."""
+    B, H, npad, d = q_i8.shape
+    info = sage_kernel_info()
+    s = torch.empty((n_q_blocks * info["block_m"], n_kv_tiles * info["kv_tile"]),
+                    dtype=torch.int32, device=q_i8.device)
+    _check(load().sage_debug_qk_i32_ex(q_i8.data_ptr(), k_i8.data_ptr(), B, H, N, d, b, h,
+                                       q_block, kv_tile, n_q_blocks, n_kv_tiles, int(mode),
+                                       s.data_ptr(), _stream(q_i8.device)))
     return s
 
 

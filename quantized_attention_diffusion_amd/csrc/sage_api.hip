@@ -445,6 +445,17 @@ SAGE_EXPORT int sage_workspace_bytes_sparse(int B, int H, int N, int d, size_t* 
   return ok();
 }
 
+SAGE_EXPORT int sage_density_schedule(int step, int n_steps, float tau_start, float tau_end, float* tau) {
+  if (!tau) return fail(SAGE_EINVAL, "tau is NULL");
+  if (n_steps < 1 || step < 0 || step >= n_steps)
+    return fail(SAGE_EINVAL, "step %d outside [0, %d)", step, n_steps);
+  if (!(isfinite(tau_start) && tau_start > 0.0f) || !(isfinite(tau_end) && tau_end > 0.0f))
+    return fail(SAGE_EINVAL, "tau_start and tau_end must be finite and > 0");
+  const double t = n_steps == 1 ? 1.0 : (double)step / (double)(n_steps - 1);
+  *tau = (float)((double)tau_start + ((double)tau_end - (double)tau_start) * t);
+  return ok();
+}
+
 SAGE_EXPORT int sage_attn_fwd_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                                      int B, int H, int N, int d, float sm_scale,
                                      const sage_strides strides[4], float density, void* stream,
@@ -510,10 +521,11 @@ SAGE_EXPORT int sage_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16
                           workspace, workspace_bytes);
 }
 
-SAGE_EXPORT int sage_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
-                                  int b, int h, int q_block, int kv_tile, int n_q_blocks, int n_kv_tiles,
-                                  int32_t* s_out, void* stream) {
+SAGE_EXPORT int sage_debug_qk_i32_ex(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                                     int b, int h, int q_block, int kv_tile, int n_q_blocks, int n_kv_tiles,
+                                     int mode, int32_t* s_out, void* stream) {
   if (int rc = check_shape(B, H, N, d)) return rc;
+  if (int rc = check_mode(mode)) return rc;
   if (!q_i8 || !k_i8 || !s_out) return fail(SAGE_EINVAL, "q_i8, k_i8 and s_out must not be NULL");
   if (!aligned(q_i8, kAlign) || !aligned(k_i8, kAlign)) return fail(SAGE_EALIGN, "q_i8/k_i8 not 256-byte aligned");
   if (!aligned(s_out, 16)) return fail(SAGE_EALIGN, "s_out is not 16-byte aligned");
@@ -523,9 +535,19 @@ SAGE_EXPORT int sage_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B,
   if (n_q_blocks < 1 || n_kv_tiles < 1 || q_block < 0 || kv_tile < 0 ||
       q_block + (int64_t)n_q_blocks > nqb || kv_tile + (int64_t)n_kv_tiles > nkt)
     return fail(SAGE_EINVAL, "tile range outside the padded operands");
-  return launch_status(sage::launch_debug_qk(q_i8, k_i8, d, npad, (int64_t)b * H + h, q_block, kv_tile,
-                                             n_q_blocks, n_kv_tiles, s_out, (hipStream_t)stream),
+  // the body sage_attn_fwd_ex launches for this mode: 32x32 for the FP8, 64-token,
+  // token-mean mode at d = 128, 16x16 otherwise
+  const bool body32 = d == 128 && mode == 0;
+  return launch_status(sage::launch_debug_qk(q_i8, k_i8, d, body32, npad, (int64_t)b * H + h, q_block,
+                                             kv_tile, n_q_blocks, n_kv_tiles, s_out, (hipStream_t)stream),
                        "debug_qk");
+}
+
+SAGE_EXPORT int sage_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                                  int b, int h, int q_block, int kv_tile, int n_q_blocks, int n_kv_tiles,
+                                  int32_t* s_out, void* stream) {
+  return sage_debug_qk_i32_ex(q_i8, k_i8, B, H, N, d, b, h, q_block, kv_tile, n_q_blocks, n_kv_tiles, 0,
+                              s_out, stream);
 }
 
 SAGE_EXPORT int sage_debug_e4m3(const float* x, uint8_t* codes, int64_t n, void* stream) {

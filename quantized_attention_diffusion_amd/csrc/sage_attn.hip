@@ -1268,13 +1268,19 @@ static void launch_attn_pair(const AttnArgs& a, unsigned grid, hipStream_t s) {
 
 template <int D, int PV, bool TOK>
 static void launch_attn_kbm(const AttnArgs& a, unsigned grid, hipStream_t s) {
-  if constexpr (PV == kPvFp8) {
-    if (a.k_bmean) {
-      launch_attn_pair<D, PV, TOK, true>(a, grid, s);
-      return;
+  if constexpr (PV == kPvFp8 && D == 128 && !TOK) {
+    // FP8 P.V with 64-token scales and the token mean runs the 32x32 body
+    // (launch_attn_d); of this mode only the block-residual form comes here
+    launch_attn_pair<D, PV, TOK, true>(a, grid, s);
+  } else {
+    if constexpr (PV == kPvFp8) {
+      if (a.k_bmean) {
+        launch_attn_pair<D, PV, TOK, true>(a, grid, s);
+        return;
+      }
     }
+    launch_attn_pair<D, PV, TOK, false>(a, grid, s);
   }
-  launch_attn_pair<D, PV, TOK, false>(a, grid, s);
 }
 
 template <int D, int PV>
@@ -1299,12 +1305,15 @@ static void launch_attn_d(const AttnArgs& a, unsigned grid, hipStream_t s) {
       return;
     }
   }
-  if (a.tile_list) {
-    if (pair_priorities(a, grid))
-      hipLaunchKernelGGL((k_attn_sparse<D, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_attn_sparse<D, false>), dim3(grid), dim3(kThreads), 0, s, a);
-    return;
+  if constexpr (D == 64) {
+    // block-sparse steps always take mode 0, which at d = 128 is the 32x32 body
+    if (a.tile_list) {
+      if (pair_priorities(a, grid))
+        hipLaunchKernelGGL((k_attn_sparse<D, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_attn_sparse<D, false>), dim3(grid), dim3(kThreads), 0, s, a);
+      return;
+    }
   }
   if (a.pv == kPvBf16) launch_attn_tok<D, kPvBf16>(a, grid, s);
   else launch_attn_tok<D, kPvFp8>(a, grid, s);
@@ -1334,11 +1343,11 @@ hipError_t launch_attn(const AttnArgs& args, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_t npad,
+hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, bool body32, int64_t npad,
                            int64_t bh, int q_block, int kv_tile, int n_q_blocks,
                            int n_kv_tiles, int32_t* s_out, hipStream_t s) {
   const dim3 grid(n_kv_tiles, n_q_blocks);
-  if (d == 128) {
+  if (d == 128 && body32) {
     hipLaunchKernelGGL(k_debug_qk32, grid, dim3(kThreads), 0, s, q_i8, k_i8, npad, bh, q_block, kv_tile,
                        n_kv_tiles, s_out);
     return hipGetLastError();
@@ -1366,8 +1375,6 @@ template __global__ void k_attn<64, kPvBf16, false, false, false>(AttnArgs);
 template __global__ void k_attn<64, kPvBf16, false, false, true>(AttnArgs);
 template __global__ void k_attn<64, kPvBf16, true, false, false>(AttnArgs);
 template __global__ void k_attn<64, kPvBf16, true, false, true>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, false, false, false>(AttnArgs);
-template __global__ void k_attn<128, kPvFp8, false, false, true>(AttnArgs);
 template __global__ void k_attn<128, kPvFp8, true, false, false>(AttnArgs);
 template __global__ void k_attn<128, kPvFp8, true, false, true>(AttnArgs);
 template __global__ void k_attn<128, kPvFp8, false, true, false>(AttnArgs);
@@ -1384,8 +1391,6 @@ template __global__ void k_attn32_sparse<false>(AttnArgs);
 template __global__ void k_attn32_sparse<true>(AttnArgs);
 template __global__ void k_attn_sparse<64, false>(AttnArgs);
 template __global__ void k_attn_sparse<64, true>(AttnArgs);
-template __global__ void k_attn_sparse<128, false>(AttnArgs);
-template __global__ void k_attn_sparse<128, true>(AttnArgs);
 template __global__ void k_debug_qk<64>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,
                                         int64_t, int, int, int, int32_t* __restrict__);
 template __global__ void k_debug_qk<128>(const int8_t* __restrict__, const int8_t* __restrict__, int64_t,

@@ -106,7 +106,8 @@ struct SelectArgs {
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_block_select(const SelectArgs& a, hipStream_t s);
-hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, int64_t npad,
+// body32: the 32x32 matrix-core body (d = 128 only), else the 16x16 one
+hipError_t launch_debug_qk(const int8_t* q_i8, const int8_t* k_i8, int d, bool body32, int64_t npad,
                            int64_t bh, int q_block, int kv_tile, int n_q_blocks,
                            int n_kv_tiles, int32_t* s_out, hipStream_t s);
 hipError_t launch_debug_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t s);

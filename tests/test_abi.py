@@ -116,6 +116,12 @@ def test_quant_and_debug_entry_points_validate(lib):
     assert rc == -1 and "tile range" in _err(lib)
     rc = lib.sage_debug_qk_i32(A, B_, 1, 2, 100, 64, 0, 5, 0, 0, 1, 1, O, None)
     assert rc == -1 and "out of range" in _err(lib)
+    rc = lib.sage_debug_qk_i32_ex(A, B_, 1, 2, 100, 128, 0, 0, 0, 0, 1, 1, 0x100, O, None)
+    assert rc == -1 and "mode" in _err(lib)
+    rc = lib.sage_debug_qk_i32_ex(A, B_, 1, 2, 100, 128, 0, 0, 0, 0, 1, 1, 5, O, None)
+    assert rc == -2 and "SAGE_K_BLOCK_MEAN" in _err(lib)        # bf16 P.V with block-residual K
+    rc = lib.sage_debug_qk_i32_ex(A, B_, 1, 2, 100, 128, 0, 0, 0, 1, 2, 1, 2, O, None)
+    assert rc == -1 and "tile range" in _err(lib)
     assert lib.sage_debug_e4m3(A, O, -1, None) == -1
     assert lib.sage_debug_e4m3(0, 0, 0, None) == 0          # nothing to do, no launch
     rc = lib.sage_attn_fwd_prequant(A, A + 4096, B_, B_ + 4096, C, C + 4096, O,
@@ -195,6 +201,29 @@ def test_sparse_entry_points_validate(lib):
     rc = lib.sage_block_select(A, A + (1 << 20), B_, B_ + (1 << 20), 1, 2, 100, 128, ctypes.c_float(0.5),
                                A + 64, C, W, 1 << 30, None)
     assert rc == -1 and "overlap" in _err(lib)
+
+
+def test_density_schedule_moves_from_sparse_to_dense(lib):
+    """The host-only schedule helper: linear in the step index from tau_start (first
+    step) to tau_end (last step), fp64 arithmetic rounded once to fp32."""
+    import numpy as np
+    import quantized_attention_diffusion_amd as sage
+    n, t0, t1 = 30, 0.25, 1.0
+    taus = [sage.sage_density_schedule(i, n, t0, t1) for i in range(n)]
+    assert taus[0] == np.float32(t0) and taus[-1] == np.float32(t1)
+    assert all(a < b for a, b in zip(taus, taus[1:]))                       # sparse early, dense late
+    want = [float(np.float32(t0 + (t1 - t0) * i / (n - 1))) for i in range(n)]
+    assert taus == want
+    assert sage.sage_density_schedule(0, 1, 0.3, 0.9) == np.float32(0.9)    # one step: the last
+    assert sage.sage_density_schedule(2, 5, 0.5, 0.5) == np.float32(0.5)    # constant
+    assert sage.sage_density_schedule(4, 5, 1.0, 0.2) == np.float32(0.2)    # any direction
+    tau = ctypes.c_float(-7.0)
+    for args in ((5, 5, 0.5, 1.0), (-1, 5, 0.5, 1.0), (0, 0, 0.5, 1.0), (0, 5, 0.0, 1.0),
+                 (0, 5, 0.5, float("inf")), (0, 5, float("nan"), 1.0)):
+        rc = lib.sage_density_schedule(args[0], args[1], ctypes.c_float(args[2]), ctypes.c_float(args[3]),
+                                       ctypes.byref(tau))
+        assert rc == -1 and tau.value == -7.0
+    assert lib.sage_density_schedule(0, 5, ctypes.c_float(0.5), ctypes.c_float(1.0), None) == -1
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

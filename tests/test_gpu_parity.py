@@ -65,12 +65,17 @@ def test_qk_int32_tiles_bit_exact(case):
     npad = gq["q_i8"].shape[2]
     info = sage.sage_kernel_info()
     nqb, nkt = npad // info["block_m"], npad // info["kv_tile"]
-    for b in range(B):
-        for h in range(H):
-            s = sage.sage_debug_qk_i32(gq["q_i8"], gq["k_i8"], N, b, h, 0, 0, nqb, nkt).cpu().numpy()
-            want = oracle.qk_int32(ref["q_i8"][b, h], ref["k_i8"][b, h])        # [N, N]
-            assert np.array_equal(s[:N, :N], want), f"S differs at head ({b}, {h})"
-            assert not s[N:, :].any() and not s[:, N:].any()                    # zero padding
+    # at d = 128 mode 0 runs the 32x32 body and the other modes the 16x16 one; the
+    # debug entry point takes the same staging and products as the body of its mode
+    modes = (0, sage.SAGE_QK_PER_TOKEN) if d == 128 else (0,)
+    for mode in modes:
+        for b in range(B):
+            for h in range(H):
+                s = sage.sage_debug_qk_i32_ex(gq["q_i8"], gq["k_i8"], N, b, h, 0, 0, nqb, nkt,
+                                              mode=mode).cpu().numpy()
+                want = oracle.qk_int32(ref["q_i8"][b, h], ref["k_i8"][b, h])        # [N, N]
+                assert np.array_equal(s[:N, :N], want), f"S differs at head ({b}, {h}), mode {mode}"
+                assert not s[N:, :].any() and not s[:, N:].any()                    # zero padding
 
 
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
