@@ -280,15 +280,28 @@ def cpu_baseline(w, rows_total: int | None = None):
                           f": {est:.1f} s per step") + "; numpy, 1 BLAS thread per process")}
 
 
+def _code_tokens(text: str) -> str:
+    """The text with C/C++ and Python comments removed and whitespace collapsed, so that
+    an edit of a comment does not count as a change of the kernel."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)         # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                      # line comments
+    text = re.sub(r"(?m)^\s*#(?!\s*(include|define|pragma|if|else|elif|endif|ifdef|ifndef|undef)\b)[^\n]*", " ",
+                  text)                                         # Python comment lines
+    text = re.sub(r'"""(.*?)"""', " ", text, flags=re.S)        # Python docstrings
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the sources and build flags that define the attention kernel; a recorded
-    traffic figure is used only while it matches."""
+    """Hash of the sources and build flags that define the attention kernel (their code
+    without comments); a recorded traffic figure is used only while it matches."""
     import hashlib
 
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,14 +13,21 @@
 // the tile's two bf16 block means are staged with the K tile, and their products with
 // the query codes, on bf16 matrix cores, enter the logits); PAIR = the issue priorities
 // that even out the two workgroups sharing a CU, chosen by the host for grids of at most
-// two rounds (IssuePriority).  The block-sparse kernel
-// (k_attn_sparse) is the FP8 body visiting only the key tiles its query block keeps
-// (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 4; the selection is in
+// two rounds (IssuePriority).  The block-sparse kernels (k_attn32_sparse at d = 128,
+// k_attn_sparse at d = 64) are the FP8 bodies visiting only the key tiles their query
+// block keeps (sd114.wiki ComfyUI-sol-attn page, "核心亮点" item 4; the selection is in
 // sage_select.hip).
 //
+// Two bodies.  The default path at d = 128 (FP8 P.V, 64-token scales, token-mean K,
+// dense and block-sparse) runs on 32x32 matrix-core tiles, one 32-query group per wave
+// (k_attn32, described at attn32_body below); every other combination runs on the
+// 16x16 tiles described here (k_attn).  Both share the workgroup shape, the LDS DMA
+// staging, the per-element softmax arithmetic and the epilogue.
+//
 // Work decomposition
-//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 2 groups of 16
-//   queries; 2 workgroups per CU (2 waves per SIMD).  Keys are visited in tiles of 128.
+//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 queries (16x16
+//   body: 2 groups of 16); 2 workgroups per CU (2 waves per SIMD).  Keys are visited in
+//   tiles of 128.
 //   K tiles (128 x d int8) and V tiles (d x 128, channel-major) are copied HBM -> LDS
 //   by LDS DMA (buffer_load_dwordx4 ... lds: no data registers, and the per-tile
 //   address advance is a scalar offset, so no vector instruction) and shared by the 4

@@ -53,7 +53,10 @@ def test_traffic_record_is_used_only_while_the_sources_match(tmp_path, monkeypat
     assert bench.kernel_source_hash() == current
     assert bench.recorded_traffic("flux_like") == rec
     assert bench.recorded_traffic("stress") is None            # no record for that workload
-    # any edit of a hashed source invalidates the record
+    # a comment or a blank line leaves the code unchanged; any edit of the code
+    # invalidates the record
     src = tmp_path / bench.ATTN_SOURCES[0]
-    src.write_bytes(src.read_bytes() + b"\n")
+    src.write_bytes(src.read_bytes() + b"\n// a comment\n/* another */\n")
+    assert bench.recorded_traffic("flux_like") == rec
+    src.write_bytes(src.read_bytes() + b"static int x;\n")
     assert bench.recorded_traffic("flux_like") is None
