@@ -99,6 +99,8 @@ def warm(fn, seconds: float) -> float:
 
 
 WARM_S = 0.5              # set from --warm-seconds
+EVICT_BYTES = 512 << 20   # written before each cold-cache quantisation call
+COLD_REPS = 9
 CPU_SHARE = 16            # worker processes at most: the host-core share of one GPU
 
 
@@ -216,9 +218,22 @@ def measure(w, steps, warmup):
     torch.cuda.synchronize(dev)
     quant_ms = e0.elapsed_time(e1) / steps
     attn_ms = e2.elapsed_time(e3) / steps
-    del q, k, v, out, ws, quant
+    # the quantisation pass with a cold memory-side cache: 512 MiB (twice the chip's
+    # 256 MiB cache) written before each timed call; median over COLD_REPS calls
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(COLD_REPS):
+        evict.fill_(1)
+        e0.record(stream)
+        sage.sage_quant_qk(q, k, v, out=quant)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        cold.append(e0.elapsed_time(e1))
+    quant_cold_ms = sorted(cold)[len(cold) // 2]
+    del q, k, v, out, ws, quant, evict
     torch.cuda.empty_cache()
     return dict(step_ms=step_ms, wall_s=wall, quant_ms=quant_ms, attn_ms=attn_ms, warm_s=warm_s,
+                quant_cold_ms=quant_cold_ms, quant_cold_gbs=quant_bytes(w) / (quant_cold_ms * 1e-3) / 1e9,
                 tops=w.ops / (step_ms * 1e-3) / 1e12,
                 attn_tops=w.ops / (attn_ms * 1e-3) / 1e12,
                 quant_gbs=quant_bytes(w) / (quant_ms * 1e-3) / 1e9)
@@ -416,7 +431,9 @@ def main():
                            "attn_tops": round(rs["attn_tops"], 2),
                            "mfma_util": round(rs["attn_tops"] / PEAK_TOPS, 4),
                            "quant_ms": round(rs["quant_ms"], 4),
-                           "quant_gbs": round(rs["quant_gbs"], 1)}
+                           "quant_gbs": round(rs["quant_gbs"], 1),
+                           "quant_cold_ms": round(rs["quant_cold_ms"], 4),
+                           "quant_cold_gbs": round(rs["quant_cold_gbs"], 1)}
         for name in MODE_SWEEP + [w.name]:
             wq = workloads.get(name)
             print(f"[bench] optional modes {name} N={wq.N}", file=sys.stderr, flush=True)
@@ -448,7 +465,9 @@ def main():
         "attn_only": {"ms": round(r["attn_ms"], 5), "tops": round(r["attn_tops"], 2),
                       "mfma_util": round(r["attn_tops"] / PEAK_TOPS, 4)},
         "quant_only": {"ms": round(r["quant_ms"], 5), "gbs": round(r["quant_gbs"], 1),
-                       "hbm_frac": round(r["quant_gbs"] / PEAK_HBM_GBS, 4)},
+                       "hbm_frac": round(r["quant_gbs"] / PEAK_HBM_GBS, 4),
+                       "cold_ms": round(r["quant_cold_ms"], 5), "cold_gbs": round(r["quant_cold_gbs"], 1),
+                       "cold_hbm_frac": round(r["quant_cold_gbs"] / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(r["attn_tops"] / PEAK_TOPS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,
