@@ -1,6 +1,7 @@
 """The entry points allocate and synchronise nothing, so a HIP graph can capture them:
-a captured dense step and a captured block-sparse step, replayed several times with
-eager work and synchronisations in between, reproduce the eager outputs bit for bit."""
+a captured dense step, a captured quality-mode step (bf16 P.V, per-token scales) and a
+captured block-sparse step, replayed several times with eager work and
+synchronisations in between, reproduce the eager outputs bit for bit."""
 import pytest
 import torch
 
@@ -14,17 +15,24 @@ def setup_module(module):
     require_gpu()
 
 
-@pytest.mark.parametrize("sparse", [False, True], ids=["dense", "sparse"])
-def test_captured_step_replays_match_eager(sparse):
+@pytest.mark.parametrize("kind", ["dense", "quality", "sparse"])
+def test_captured_step_replays_match_eager(kind):
     B, N, H, d = 1, 1000, 2, 128
     q, k, v = (t.cuda() for t in random_qkv(B, N, H, d, 31, 2))
-    nbytes = sage.sage_workspace_bytes_sparse(B, H, N, d) if sparse else sage.sage_workspace_bytes(B, H, N, d)
+    if kind == "sparse":
+        nbytes = sage.sage_workspace_bytes_sparse(B, H, N, d)
+    elif kind == "quality":
+        nbytes = sage.sage_workspace_bytes_ex(B, H, N, d, sage.mode_bits("bf16", per_token=True))
+    else:
+        nbytes = sage.sage_workspace_bytes(B, H, N, d)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
 
     def step():
-        if sparse:
+        if kind == "sparse":
             sage.sage_attn_fwd_sparse(q, k, v, 0.5, out=out, workspace=ws)
+        elif kind == "quality":
+            sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, pv="bf16", per_token=True)
         else:
             sage.sage_attn_fwd(q, k, v, out=out, workspace=ws)
 

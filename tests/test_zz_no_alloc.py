@@ -45,6 +45,34 @@ def test_noalloc_strided_views_and_sm_scale():
     assert _same(got, want)
 
 
+def test_noalloc_step_captured_in_a_graph():
+    # the callers this entry point is for capture it in a HIP graph: replays, with eager
+    # calls and synchronisations between them, give the eager output bit for bit
+    q, k, v = (t.cuda() for t in random_qkv(1, 1000, 2, 128, 54, 2))
+    out = torch.empty_like(q)
+    sage.sage_attn_fwd_noalloc(q, k, v, out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sage.sage_attn_fwd_noalloc(q, k, v, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sage.sage_attn_fwd_noalloc(q, k, v, out)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(out, eager), f"replay {i}"
+        sage.sage_attn_fwd_noalloc(q, k, v, out)
+        torch.cuda.synchronize()
+        assert _same(out, eager), f"eager after replay {i}"
+
+
 def test_noalloc_rejects_a_shape_beyond_its_array():
     q, k, v = (torch.zeros(1, 8192, 24, 128, dtype=torch.bfloat16, device="cuda") for _ in range(3))
     with pytest.raises(sage.SageError, match="no-allocation"):
