@@ -93,6 +93,31 @@ def test_fwd_rejects_bad_arguments_before_any_hip_call(lib, kw, status, msg):
     assert msg in _err(lib)
 
 
+def test_error_text_is_per_thread(lib):
+    """sage_last_error is thread-local: threads that fail different checks at the same
+    time each read back their own message."""
+    import threading
+    cases = [(dict(N=0), "must be >= 1"), (dict(sm=-1.0), "sm_scale"), (dict(q=A + 8), "16-byte aligned"),
+             (dict(ws=0), "workspace is NULL")]
+    bad = []
+    barrier = threading.Barrier(len(cases))
+
+    def worker(kw, msg):
+        barrier.wait()
+        for _ in range(200):
+            _fwd(lib, **kw)
+            if msg not in _err(lib):
+                bad.append((msg, _err(lib)))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad
+
+
 def test_fwd_rejects_misaligned_and_overlapping_strides(lib):
     N, H, d = 100, 2, 128
     bad = [_st(N * H * d, d, H * d + 4)] * 4
