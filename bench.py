@@ -14,6 +14,7 @@ low.  The time spent is reported as "warm_s".
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S] [--workload NAME]
                 [--no-sweep] [--no-cpu-baseline] [--pmc-run] [--sparse-run WORKLOADS]
+                [--modes-run WORKLOADS]
 """
 from __future__ import annotations
 
@@ -67,6 +68,9 @@ def _parse():
                     help="only run the block-sparse step a few times at each bench density on "
                          "the comma-separated workloads (the program a rocprofv3 kernel trace "
                          "of the tile selection profiles)")
+    ap.add_argument("--modes-run", metavar="WORKLOADS", default=None,
+                    help="only run each optional mode's step a few times on the comma-separated "
+                         "workloads (the program a rocprofv3 kernel trace of the mode kernels profiles)")
     return ap.parse_args()
 
 
@@ -387,6 +391,32 @@ def sparse_run(names: str):
         torch.cuda.empty_cache()
 
 
+def modes_run(names: str):
+    """Steps of each optional mode (MODES, then FP8 P.V with per-token scales) for a
+    kernel trace: per workload and mode, untimed steps for 0.3 s (clocks up), then 5
+    steps (3 at 64K tokens and more) into a preallocated workspace."""
+    import torch
+    import workloads
+    import quantized_attention_diffusion_amd as sage
+
+    modes = dict(MODES, fp8_pv_per_token=dict(pv="fp8", per_token=True))
+    for name in names.split(","):
+        w = workloads.get(name)
+        q, k, v = (t.cuda() for t in workloads.make_qkv(w))
+        out = torch.empty_like(q)
+        for mname, opts in modes.items():
+            mode = sage.mode_bits(opts.get("pv", "fp8"), opts.get("per_token", False), opts.get("k_block_mean", False))
+            ws = torch.empty(sage.sage_workspace_bytes_ex(w.B, w.H, w.N, w.d, mode), dtype=torch.uint8, device="cuda")
+            warm(lambda: sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, **opts), 0.3)
+            for _ in range(5 if w.N < 60000 else 3):
+                sage.sage_attn_fwd_ex(q, k, v, out=out, workspace=ws, **opts)
+            torch.cuda.synchronize()
+            print(f"[bench] modes run {name} {mname} done", file=sys.stderr, flush=True)
+            del ws
+        del q, k, v, out
+        torch.cuda.empty_cache()
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -402,7 +432,7 @@ def main():
     # The CPU baseline runs first, in worker processes started before this process
     # touches the GPU.
     cpu = None
-    if not args.no_cpu_baseline and not args.pmc_run and not args.sparse_run:
+    if not args.no_cpu_baseline and not args.pmc_run and not args.sparse_run and not args.modes_run:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
         print(f"[bench] cpu baseline done: {cpu['sample']}", file=sys.stderr, flush=True)
@@ -419,6 +449,9 @@ def main():
         return
     if args.sparse_run:
         sparse_run(args.sparse_run)
+        return
+    if args.modes_run:
+        modes_run(args.modes_run)
         return
     # The longer sequences run first (they also bring the GPU to its working clocks);
     # the headline workload is timed last.
