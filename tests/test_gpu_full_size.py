@@ -83,6 +83,33 @@ def test_offsets_beyond_int32():
     torch.cuda.empty_cache()
 
 
+def test_maximum_sequence_length():
+    # N = 2^22, the longest sequence the library accepts (one token more is refused):
+    # the quantised operands bit-exact (every scale, the K mean, all V codes, sampled Q
+    # and K code blocks), and sampled rows (the first, the last and two between) against
+    # the oracle's plain reading
+    B, H, N, d = 1, 1, 1 << 22, 64
+    with pytest.raises(sage.SageError):
+        sage.sage_workspace_bytes(B, H, N + 1, d)
+    print(f"[max N] B={B} H={H} N={N} d={d}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(78)
+    q = torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = (torch.randn((B, N, H, d), generator=g, device="cuda")
+         + 3.0 * torch.randn((H, d), generator=g, device="cuda")).to(torch.bfloat16)
+    v = torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = sage.sage_attn_fwd(q, k, v)
+    gq = sage.sage_quant_qk(q, k, v)
+    torch.cuda.synchronize()
+    qh, kh, vh = (t.float().cpu().numpy() for t in (q, k, v))
+    ref = oracle.quantize(qh, kh, vh)
+    compare_quant(gq, ref, N, blocks=[0, 1, N // 128, N // 64 - 1])
+    rows = np.array([0, 1, N // 2 + 5, N - 1])
+    err, _, _ = check_oracle(to_np(out[:, rows]), "max N", qh, kh, vh, rows=rows, quant=ref, readings=("fp64",))
+    print(f"    max|gpu-pipe| = {err:.2e}", flush=True)
+    del q, k, v, out, gq
+    torch.cuda.empty_cache()
+
+
 def _full_size_parity(w):
     name = w.name
     print(f"[full] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
