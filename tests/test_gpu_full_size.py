@@ -110,6 +110,32 @@ def test_maximum_sequence_length():
     torch.cuda.empty_cache()
 
 
+def test_maximum_head_count():
+    # B = 1 with H = 65535 heads (the largest grid dimension the quantisation kernels
+    # launch; H = 65536 is refused), a ragged N: the dense and the block-sparse step on
+    # sampled heads, including the last
+    B, H, N, d = 1, 65535, 200, 64
+    with pytest.raises(sage.SageError):
+        sage.sage_workspace_bytes(B, H + 1, N, d)
+    print(f"[max H] B={B} H={H} N={N} d={d}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(79)
+    q = torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = (torch.randn((B, N, H, d), generator=g, device="cuda")
+         + 3.0 * torch.randn((H, d), generator=g, device="cuda")).to(torch.bfloat16)
+    v = torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = sage.sage_attn_fwd(q, k, v)
+    sparse = sage.sage_attn_fwd_sparse(q, k, v, 0.5)
+    torch.cuda.synchronize()
+    for h in (0, 12345, H - 1):
+        qh, kh, vh = (t[:, :, h:h + 1].float().cpu().numpy() for t in (q, k, v))
+        ref = oracle.quantize(qh, kh, vh)
+        check_oracle(to_np(out[:, :, h:h + 1]), f"max H dense head {h}", qh, kh, vh, quant=ref)
+        _, tiles = oracle.select_tiles(ref, 0.5)
+        check_oracle(to_np(sparse[:, :, h:h + 1]), f"max H sparse head {h}", qh, kh, vh, quant=ref, tiles=tiles)
+    del q, k, v, out, sparse
+    torch.cuda.empty_cache()
+
+
 def _full_size_parity(w):
     name = w.name
     print(f"[full] {name} B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
