@@ -2,8 +2,6 @@
 comparisons.  Expected values come only from the oracle package."""
 from __future__ import annotations
 
-import math
-
 import numpy as np
 import torch
 

@@ -6,8 +6,6 @@ import os
 import subprocess
 import sys
 
-import pytest
-
 import bench
 import workloads
 

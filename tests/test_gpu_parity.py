@@ -1,8 +1,6 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI: quantised
 operands bit-exact, int32 Q.K^T tiles bit-exact, attention output within the
 max-abs bound of the oracle's quantised pipeline, on small and ragged shapes."""
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -10,7 +8,7 @@ import torch
 import oracle
 import workloads
 import quantized_attention_diffusion_amd as sage
-from gpu_helpers import (require_gpu, to_np, random_qkv, compare_quant, check_attention, check_oracle)
+from gpu_helpers import (require_gpu, to_np, random_qkv, compare_quant, check_oracle)
 
 pytestmark = pytest.mark.gpu
 

@@ -4,7 +4,6 @@ import math
 import os
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import e4m3_decode, e4m3_encode, e4m3_table, E4M3_MAX

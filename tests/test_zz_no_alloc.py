@@ -2,7 +2,6 @@
 its workspace in the library's device array), through the C ABI: its output must be
 bit-identical to sage_attn_fwd's on the same inputs, on two calls in a row of which the
 second is smaller, so the second runs on what the first left in the array."""
-import numpy as np
 import pytest
 import torch
 
