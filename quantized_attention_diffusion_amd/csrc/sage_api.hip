@@ -66,7 +66,7 @@ Extent extent(const void* p, const sage_strides& s, int B, int H, int N, int d) 
 
 bool overlaps(const Extent& a, const Extent& b) { return a.lo < b.hi && b.lo < a.hi; }
 
-int check_view(const char* name, const void* p, const sage_strides* s, int B, int H, int N, int d) {
+int check_view(const char* name, const void* p, const sage_strides* s) {
   if (!p) return fail(SAGE_EINVAL, "%s is NULL", name);
   if (!s) return fail(SAGE_EINVAL, "strides of %s are NULL", name);
   if (!aligned(p, 16)) return fail(SAGE_EALIGN, "%s is not 16-byte aligned", name);
@@ -244,9 +244,9 @@ static int validate_quant_inputs(const uint16_t* q, const uint16_t* k, const uin
                                  const sage_strides* sq, const sage_strides* sk,
                                  const sage_strides* sv, int B, int H, int N, int d) {
   if (int rc = check_shape(B, H, N, d)) return rc;
-  if (int rc = check_view("q", q, sq, B, H, N, d)) return rc;
-  if (int rc = check_view("k", k, sk, B, H, N, d)) return rc;
-  if (int rc = check_view("v", v, sv, B, H, N, d)) return rc;
+  if (int rc = check_view("q", q, sq)) return rc;
+  if (int rc = check_view("k", k, sk)) return rc;
+  if (int rc = check_view("v", v, sv)) return rc;
   return SAGE_OK;
 }
 
@@ -318,7 +318,7 @@ SAGE_EXPORT int sage_attn_fwd_prequant(const int8_t* q_i8, const float* q_scale,
     if (!ins[i]) return fail(SAGE_EINVAL, "%s is NULL", names[i]);
     if (!aligned(ins[i], kAlign)) return fail(SAGE_EALIGN, "%s is not 256-byte aligned", names[i]);
   }
-  if (int rc = check_view("out", out, so, B, H, N, d)) return rc;
+  if (int rc = check_view("out", out, so)) return rc;
   if (int rc = check_no_self_overlap("out", *so, B, H, N, d)) return rc;
   const Extent eo = extent(out, *so, B, H, N, d);
   for (int i = 0; i < 6; ++i)
@@ -349,7 +349,7 @@ static int validate_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   }
   if (!strides) return fail(SAGE_EINVAL, "strides is NULL");
   if (int rc = validate_quant_inputs(q, k, v, &strides[0], &strides[1], &strides[2], B, H, N, d)) return rc;
-  if (int rc = check_view("out", out, &strides[3], B, H, N, d)) return rc;
+  if (int rc = check_view("out", out, &strides[3])) return rc;
   if (int rc = check_no_self_overlap("out", strides[3], B, H, N, d)) return rc;
   const Extent eo = extent(out, strides[3], B, H, N, d);
   const void* ins[3] = {q, k, v};

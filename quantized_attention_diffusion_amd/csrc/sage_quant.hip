@@ -93,7 +93,7 @@ __device__ __forceinline__ void load_block(const uint16_t* base, int64_t stride_
 template <int D, bool NEED_V, bool TOK, bool NEED_KSUM>
 __global__ __launch_bounds__(256) void k_quant_q_stats(
     const uint16_t* __restrict__ q, Strides sq, const uint16_t* __restrict__ k, Strides sk,
-    const uint16_t* __restrict__ v, Strides sv, int H, int N, int64_t npad, int blocks_per_chunk,
+    const uint16_t* __restrict__ v, Strides sv, int N, int64_t npad, int blocks_per_chunk,
     int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
     double* __restrict__ ksum_part, float* __restrict__ vmax_part) {
   constexpr int TPR = D / 8;        // threads per token row, 8 channels each
@@ -230,7 +230,7 @@ __device__ __forceinline__ int64_t kv_work_item(int64_t lin, int64_t total) {
 template <int D, bool V16, bool TOK, bool KBM>
 __global__ __launch_bounds__(256) void k_quant_kv(
     const uint16_t* __restrict__ k, Strides sk, const uint16_t* __restrict__ v, Strides sv,
-    int H, int N, int64_t npad, uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
+    int N, int64_t npad, uint16_t* __restrict__ k_mean, const float* __restrict__ v_inv,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, uint8_t* __restrict__ v_f8,
     uint16_t* __restrict__ v16) {
   constexpr int TPR = D / 8;
@@ -387,13 +387,13 @@ static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   const int per = stats_blocks_per_chunk(a.npad);
   const int chunks = stats_chunks(a.N);
   hipLaunchKernelGGL((k_quant_q_stats<D, !V16, TOK, !KBM>), dim3(chunks, a.H, a.B), dim3(256), 0, s,
-                     a.q, a.sq, a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, per,
+                     a.q, a.sq, a.k, a.sk, a.v, a.sv, a.N, a.npad, per,
                      a.q_i8, a.q_scale, a.ksum_part, a.vmax_part);
   if constexpr (!V16 || !KBM)
     hipLaunchKernelGGL((k_quant_finalize<D, !V16, !KBM>), dim3(a.B * a.H), dim3(kFinalizeThreads), 0, s,
                        a.ksum_part, a.vmax_part, chunks, a.N, a.k_mean, a.v_scale, a.v_inv);
   hipLaunchKernelGGL((k_quant_kv<D, V16, TOK, KBM>), dim3((unsigned)(a.npad / kQuantBlock), a.H, a.B), dim3(256), 0, s,
-                     a.k, a.sk, a.v, a.sv, a.H, a.N, a.npad, a.k_mean, a.v_inv,
+                     a.k, a.sk, a.v, a.sv, a.N, a.npad, a.k_mean, a.v_inv,
                      a.k_i8, a.k_scale, a.v_f8, a.v16);
   return hipGetLastError();
 }
