@@ -403,7 +403,7 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
     nb[gq] = BM ? e[gq] + (log2_pscale - m_new[gq]) : log2_pscale - m_new[gq];
     alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
   }
-  float ls[G][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float ls[G][4];   // partial row sums, started from the first sub-tile's p (p >= 0, so 0 + p = p)
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
 #pragma unroll
@@ -412,7 +412,7 @@ __device__ __forceinline__ void softmax_tile(v4i (&S)[G][8], const float (&c)[G]
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_to_f32(S[gq][kt][i]), c[gq], nb[gq]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
+      for (int i = 0; i < 4; ++i) ls[gq][i] = kt == 0 ? p[i] : ls[gq][i] + p[i];
       store_p<PV>(P[gq], kt, p);
     }
   }
@@ -489,7 +489,7 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const uint8_t* 
     nb[gq] = BM ? e[gq] + (log2_pscale - m_new[gq]) : log2_pscale - m_new[gq];
     alpha[gq] = __builtin_amdgcn_exp2f(m[gq] - m_new[gq]);
   }
-  float ls[G][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float ls[G][4];   // partial row sums, started from the first sub-tile's p (p >= 0, so 0 + p = p)
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
 #pragma unroll
@@ -501,7 +501,7 @@ __device__ __forceinline__ void softmax_tile_tok(v4i (&S)[G][8], const uint8_t* 
         if constexpr (MASKED) p[i] = (4 * kt + i) < nvalid - 32 * g ? p[i] : 0.0f;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ls[gq][i] += p[i];
+      for (int i = 0; i < 4; ++i) ls[gq][i] = kt == 0 ? p[i] : ls[gq][i] + p[i];
       store_p<PV>(P[gq], kt, p);
     }
   }
@@ -1030,7 +1030,7 @@ __device__ __forceinline__ float softmax32(v16i (&S)[4], const float (&c_in)[2],
   const float m_new = fmaxf(m, sl);
   const float nb = log2_pscale - m_new;
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  float ls[4];      // partial row sums, started from the first p (p >= 0, so 0 + p = p)
 #pragma unroll
   for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
@@ -1043,7 +1043,7 @@ __device__ __forceinline__ float softmax32(v16i (&S)[4], const float (&c_in)[2],
           const int v = S[2 * ps + u][4 * i4 + t];
           const float x = MASKED ? __builtin_bit_cast(float, v) : s_to_f32(v);
           p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c[ps], nb));
-          ls[t] += p[t];
+          ls[t] = (ps == 0 && u == 0 && i4 == 0) ? p[t] : ls[t] + p[t];
         }
         const int w = 4 * u + i4;          // P word: keys 4w .. 4w+3 of the half
         int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[ps][w], false);
