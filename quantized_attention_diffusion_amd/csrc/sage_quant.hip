@@ -99,7 +99,11 @@ __global__ __launch_bounds__(256) void k_quant_q_stats(
   constexpr int TPR = D / 8;        // threads per token row, 8 channels each
   constexpr int RPI = 256 / TPR;    // token rows per sweep of the workgroup
   constexpr int RPT = kQuantBlock / RPI;
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // heads fastest in the workgroup order: the workgroups that run together read all
+  // heads of the same token rows, which lie together in a [B, N, H, d] tensor
+  // (measured 1-3% off the pass)
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int chunk = lin / gridDim.y, h = lin % gridDim.y, b = blockIdx.z;
   const int t = threadIdx.x, r = t / TPR, cg = t % TPR;
   const int64_t bh = (int64_t)b * gridDim.y + h;
   const int64_t nblk = npad / kQuantBlock;
@@ -239,8 +243,8 @@ __global__ __launch_bounds__(256) void k_quant_kv(
   constexpr int VW = kQuantBlock / 4 + 1;  // LDS words per channel row (odd pitch)
   const int64_t work = kv_work_item(blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z),
                                     (int64_t)gridDim.x * gridDim.y * gridDim.z);
-  const int blk = (int)(work % gridDim.x);
-  const int h = (int)((work / gridDim.x) % gridDim.y);
+  const int h = (int)(work % gridDim.y);                     // heads fastest, as in pass 1
+  const int blk = (int)((work / gridDim.y) % gridDim.x);
   const int b = (int)(work / ((int64_t)gridDim.x * gridDim.y));
   const int t = threadIdx.x, r = t / TPR, cg = t % TPR;
   const int64_t bh = (int64_t)b * gridDim.y + h;
